@@ -1,0 +1,376 @@
+// C ABI of libsparge (declared in include/sparge.h): argument validation,
+// workspace planning and the launch sequence of each entry point.  Every check
+// runs before any HIP call, so argument errors never touch the device.
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/sparge.h"
+#include "sparge_internal.hpp"
+
+namespace sparge {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Workspace plan_workspace(const Dims& d, int dtype) {
+  Workspace w{};
+  const size_t BH = (size_t)d.B * d.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
+  w.qsum = take(BH * d.nQ * d.D * sizeof(double));
+  w.qsim = take(BH * d.nQ * sizeof(double));
+  w.ksum = take(BH * d.nK * d.D * sizeof(double));
+  w.ksim = take(BH * d.nK * sizeof(double));
+  w.scores = take(BH * d.nQ * d.nK * sizeof(double));
+  w.lists = take(BH * d.nQ * d.nK * sizeof(uint16_t));
+  w.counts = take(BH * d.nQ * sizeof(int));
+  w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
+  w.kscale = take(BH * d.nK * sizeof(float));
+  w.kbar = take(BH * d.nK * d.D * sizeof(float));
+  w.conv = take(dtype == kF32 ? 3 * BH * (size_t)d.N * d.D * sizeof(uint16_t) : 0);
+  w.counters = take(8 * sizeof(unsigned long long));
+  w.total = off;
+  return w;
+}
+
+}  // namespace sparge
+
+using namespace sparge;
+
+namespace {
+
+constexpr int64_t kMaxN = 262144;  // uint16 block lists and the selector's LDS bound N
+
+sparge_status check_tensor(const sparge_tensor* t) {
+  if (!t || !t->data) return SPARGE_E_NULL;
+  if (t->dtype != SPARGE_F32 && t->dtype != SPARGE_F16 && t->dtype != SPARGE_BF16)
+    return SPARGE_E_DTYPE;
+  if (t->reserved != 0) return SPARGE_E_ARG;
+  if (t->B < 1 || t->H < 1 || t->N < 1 || t->N > kMaxN) return SPARGE_E_SHAPE;
+  if (t->D != 64 && t->D != 128) return SPARGE_E_SHAPE;
+  if (t->B * t->H * ((t->N + 127) / 128) > 0x7fffffffll) return SPARGE_E_SHAPE;
+  const int64_t es = t->dtype == SPARGE_F32 ? 4 : 2;
+  if (((uintptr_t)t->data) % 16 != 0) return SPARGE_E_UNSUPPORTED;
+  if (t->sB < 0 || t->sH < 0 || t->sN < 0) return SPARGE_E_UNSUPPORTED;
+  if ((t->sB * es) % 16 || (t->sH * es) % 16 || (t->sN * es) % 16) return SPARGE_E_UNSUPPORTED;
+  return SPARGE_OK;
+}
+
+bool same_shape(const sparge_tensor* a, const sparge_tensor* b) {
+  return a->B == b->B && a->H == b->H && a->N == b->N && a->D == b->D;
+}
+
+Dims dims_of(const sparge_tensor* t) {
+  Dims d;
+  d.B = (int)t->B; d.H = (int)t->H; d.N = (int)t->N; d.D = (int)t->D;
+  d.nQ = (d.N + 127) / 128;
+  d.nK = (d.N + 63) / 64;
+  return d;
+}
+
+View view_of(const sparge_tensor* t) { return View{t->data, t->sB, t->sH, t->sN}; }
+
+sparge_status check_opts(const sparge_opts* o) {
+  if (!o) return SPARGE_OK;
+  if (o->reserved != 0) return SPARGE_E_ARG;
+  if (!(o->scale >= 0.0) || isinf(o->scale)) return SPARGE_E_ARG;
+  if (isnan(o->sim_threshold) || isnan(o->filter_lambda)) return SPARGE_E_ARG;
+  if (o->filter_lambda > 0.0) return SPARGE_E_ARG;
+  return SPARGE_OK;
+}
+
+sparge_status check_qkv(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
+                        const sparge_tensor* out) {
+  sparge_status st;
+  if ((st = check_tensor(q)) != SPARGE_OK) return st;
+  if ((st = check_tensor(k)) != SPARGE_OK) return st;
+  if (v && (st = check_tensor(v)) != SPARGE_OK) return st;
+  if (out && (st = check_tensor(out)) != SPARGE_OK) return st;
+  if (k->dtype != q->dtype || (v && v->dtype != q->dtype) || (out && out->dtype != q->dtype))
+    return SPARGE_E_DTYPE;
+  if (!same_shape(q, k) || (v && !same_shape(q, v)) || (out && !same_shape(q, out)))
+    return SPARGE_E_SHAPE;
+  if (out && (out->data == q->data || out->data == k->data || (v && out->data == v->data)))
+    return SPARGE_E_ARG;
+  return SPARGE_OK;
+}
+
+struct Ctx {
+  Dims d;
+  Workspace w;
+  char* ws;
+  hipStream_t s;
+  unsigned long long* counters;  // nullable
+  template <typename T>
+  T* at(size_t off) const { return (T*)(ws + off); }
+};
+
+#define SPARGE_TRY(expr) do { const hipError_t e__ = (expr); if (e__ != hipSuccess) return SPARGE_E_HIP; } while (0)
+
+sparge_status begin_stats(Ctx& c, const sparge_opts* o) {
+  c.counters = nullptr;
+  if (o && o->prof_start) SPARGE_TRY(hipEventRecord((hipEvent_t)o->prof_start, c.s));
+  if (o && o->stats) {
+    c.counters = c.at<unsigned long long>(c.w.counters);
+    SPARGE_TRY(hipMemsetAsync(c.counters, 0, 8 * sizeof(unsigned long long), c.s));
+  }
+  return SPARGE_OK;
+}
+
+sparge_status end_stats(Ctx& c, const sparge_opts* o) {
+  if (!c.counters) return SPARGE_OK;
+  unsigned long long h[8];
+  SPARGE_TRY(hipMemcpyAsync(h, c.counters, sizeof(h), hipMemcpyDeviceToHost, c.s));
+  SPARGE_TRY(hipStreamSynchronize(c.s));
+  o->stats->valid_blocks = h[0];
+  o->stats->kept_blocks = h[1];
+  o->stats->group_updates = h[2];
+  o->stats->skipped_updates = h[3];
+  return SPARGE_OK;
+}
+
+// The attention operands: 16-bit views (fp32 inputs are rounded into the workspace).
+struct Operands {
+  View q, k, v;
+  int in_f16;
+  int dtype16;
+};
+
+sparge_status prepare_operands(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
+                               const sparge_tensor* v, Operands& op) {
+  if (q->dtype == SPARGE_F32) {
+    const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
+    uint16_t* base = c.at<uint16_t>(c.w.conv);
+    const sparge_tensor* src[3] = {q, k, v};
+    View* dst[3] = {&op.q, &op.k, &op.v};
+    for (int x = 0; x < 3; ++x) {
+      uint16_t* o = base + x * one;
+      SPARGE_TRY(launch_convert_bf16(view_of(src[x]), c.d, o, c.s));
+      *dst[x] = View{o, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
+    }
+    op.in_f16 = 0;
+    op.dtype16 = kBF16;
+  } else {
+    op.q = view_of(q);
+    op.k = view_of(k);
+    op.v = view_of(v);
+    op.in_f16 = q->dtype == SPARGE_F16;
+    op.dtype16 = q->dtype;
+  }
+  return SPARGE_OK;
+}
+
+sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out,
+                            const sparge_opts& o, int causal, int filter_on) {
+  AttnParams p{};
+  p.q = op.q;
+  p.k = op.k;
+  p.v = op.v;
+  p.o = out->data;
+  p.osB = out->sB;
+  p.osH = out->sH;
+  p.osN = out->sN;
+  p.in_f16 = op.in_f16;
+  p.out_type = out->dtype;
+  p.causal = causal;
+  p.filter_on = filter_on;
+  p.qk_int8 = o.qk_int8 != 0;
+  p.pv_fp16 = o.pv_fp16 != 0;
+  const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
+  const double log2e = 1.4426950408889634;
+  p.c = (float)(scale * log2e);
+  p.lam2 = (float)(o.filter_lambda * log2e);
+  p.lists = c.at<uint16_t>(c.w.lists);
+  p.counts = c.at<int>(c.w.counts);
+  p.counters = c.counters;
+  if (p.qk_int8) {
+    int8_t* k8 = c.at<int8_t>(c.w.k8);
+    float* ks = c.at<float>(c.w.kscale);
+    float* kb = c.at<float>(c.w.kbar);
+    SPARGE_TRY(launch_quant_k(op.k, op.dtype16, c.d, k8, c.d.D, (int64_t)c.d.nK * 64 * c.d.D, ks,
+                              kb, c.s));
+    p.k8 = k8;
+    p.kscale = ks;
+    p.kbar = kb;
+  }
+  if (o.prof_attn_begin) SPARGE_TRY(hipEventRecord((hipEvent_t)o.prof_attn_begin, c.s));
+  SPARGE_TRY(launch_sparse_attn(p, c.d, c.s));
+  if (o.prof_attn_end) SPARGE_TRY(hipEventRecord((hipEvent_t)o.prof_attn_end, c.s));
+  return SPARGE_OK;
+}
+
+sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor* k, double topk,
+                            int causal, const sparge_opts& o, uint8_t* mask_out) {
+  const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
+  double* qsum = c.at<double>(c.w.qsum);
+  double* qsim = c.at<double>(c.w.qsim);
+  double* ksum = c.at<double>(c.w.ksum);
+  double* ksim = c.at<double>(c.w.ksim);
+  double* scores = c.at<double>(c.w.scores);
+  SPARGE_TRY(launch_block_stats(view_of(q), view_of(k), q->dtype, c.d, qsum, qsim, ksum, ksim, c.s));
+  SPARGE_TRY(launch_pooled_scores(qsum, ksum, c.d, causal, scale, scores, c.s));
+  SPARGE_TRY(launch_select(scores, qsim, ksim, c.d, causal, topk, o.sim_threshold, mask_out,
+                           c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts), c.counters, c.s));
+  return SPARGE_OK;
+}
+
+sparge_status init_ctx(Ctx& c, const sparge_tensor* q, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  c.d = dims_of(q);
+  c.w = plan_workspace(c.d, q->dtype);
+  if (!workspace) return SPARGE_E_WORKSPACE;
+  if (workspace_bytes < c.w.total) return SPARGE_E_WORKSPACE;
+  if (((uintptr_t)workspace) % 256 != 0) return SPARGE_E_UNSUPPORTED;
+  c.ws = (char*)workspace;
+  c.s = (hipStream_t)stream;
+  c.counters = nullptr;
+  return SPARGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void sparge_default_opts(sparge_opts* o) {
+  if (!o) return;
+  memset(o, 0, sizeof(*o));
+  o->scale = 0.0;
+  o->sim_threshold = 0.1;
+  o->filter_lambda = -10.0;
+  o->filter_on = 1;
+  o->qk_int8 = 0;
+  o->pv_fp16 = 0;
+}
+
+size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t dtype,
+                              const sparge_opts* opts) {
+  (void)opts;
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN || (D != 64 && D != 128)) return 0;
+  if (dtype != SPARGE_F32 && dtype != SPARGE_F16 && dtype != SPARGE_BF16) return 0;
+  Dims d;
+  d.B = (int)B; d.H = (int)H; d.N = (int)N; d.D = (int)D;
+  d.nQ = (d.N + 127) / 128;
+  d.nK = (d.N + 63) / 64;
+  return plan_workspace(d, dtype).total;
+}
+
+sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
+                               const sparge_tensor* v, const sparge_tensor* out, double topk,
+                               int32_t is_causal, const sparge_opts* opts, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  sparge_status st;
+  if ((st = check_qkv(q, k, v, out)) != SPARGE_OK) return st;
+  if ((st = check_opts(opts)) != SPARGE_OK) return st;
+  if (!(topk > 0.0 && topk <= 1.0)) return SPARGE_E_ARG;
+  sparge_opts o;
+  if (opts) o = *opts; else sparge_default_opts(&o);
+  Ctx c;
+  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  Operands op;
+  if ((st = prepare_operands(c, q, k, v, op)) != SPARGE_OK) return st;
+  if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
+  if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0)) != SPARGE_OK) return st;
+  return end_stats(c, &o);
+}
+
+sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
+                                const sparge_tensor* v, const uint8_t* mask_id,
+                                const sparge_tensor* out, const sparge_opts* opts, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sparge_status st;
+  if ((st = check_qkv(q, k, v, out)) != SPARGE_OK) return st;
+  if ((st = check_opts(opts)) != SPARGE_OK) return st;
+  sparge_opts o;
+  if (opts) {
+    o = *opts;
+  } else {
+    sparge_default_opts(&o);
+    o.filter_on = 0;
+  }
+  Ctx c;
+  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  Operands op;
+  if ((st = prepare_operands(c, q, k, v, op)) != SPARGE_OK) return st;
+  SPARGE_TRY(launch_compact(mask_id, c.d, c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts),
+                            c.counters, c.s));
+  if ((st = run_attention(c, op, out, o, 0, o.filter_on != 0)) != SPARGE_OK) return st;
+  return end_stats(c, &o);
+}
+
+sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k, double topk,
+                                  int32_t is_causal, const sparge_opts* opts, uint8_t* mask_out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  sparge_status st;
+  if ((st = check_qkv(q, k, nullptr, nullptr)) != SPARGE_OK) return st;
+  if ((st = check_opts(opts)) != SPARGE_OK) return st;
+  if (!mask_out) return SPARGE_E_NULL;
+  if (!(topk > 0.0 && topk <= 1.0)) return SPARGE_E_ARG;
+  sparge_opts o;
+  if (opts) o = *opts; else sparge_default_opts(&o);
+  Ctx c;
+  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, mask_out)) != SPARGE_OK) return st;
+  return end_stats(c, &o);
+}
+
+sparge_status sparge_quantize_qk(const sparge_tensor* q, const sparge_tensor* k, int8_t* q_codes,
+                                 float* q_scales, int8_t* k_codes, float* k_scales, float* k_means,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  sparge_status st;
+  if ((st = check_qkv(q, k, nullptr, nullptr)) != SPARGE_OK) return st;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !k_means) return SPARGE_E_NULL;
+  Ctx c;
+  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  SPARGE_TRY(launch_quant_q(view_of(q), q->dtype, c.d, q_codes, q_scales, c.s));
+  SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,
+                            k_scales, k_means, c.s));
+  return SPARGE_OK;
+}
+
+sparge_status sparge_hilbert_perm3d(int32_t T, int32_t Hg, int32_t W, int32_t* perm_host) {
+  if (!perm_host) return SPARGE_E_NULL;
+  if (T < 1 || Hg < 1 || W < 1) return SPARGE_E_SHAPE;
+  if ((int64_t)T * Hg * W > (1ll << 30) || T > (1 << 20) || Hg > (1 << 20) || W > (1 << 20))
+    return SPARGE_E_SHAPE;
+  hilbert_perm3d_host(T, Hg, W, perm_host);
+  return SPARGE_OK;
+}
+
+sparge_status sparge_reorder(const sparge_tensor* x, const sparge_tensor* y, const int32_t* perm,
+                             int64_t offset, int64_t count, int32_t inverse, void* stream) {
+  sparge_status st;
+  if ((st = check_tensor(x)) != SPARGE_OK) return st;
+  if ((st = check_tensor(y)) != SPARGE_OK) return st;
+  if (x->dtype != y->dtype) return SPARGE_E_DTYPE;
+  if (!same_shape(x, y)) return SPARGE_E_SHAPE;
+  if (x->data == y->data) return SPARGE_E_ARG;
+  if (count < 0 || offset < 0 || offset + count > x->N) return SPARGE_E_ARG;
+  if (count > 0 && !perm) return SPARGE_E_NULL;
+  const Dims d = dims_of(x);
+  const int es = x->dtype == SPARGE_F32 ? 4 : 2;
+  SPARGE_TRY(launch_reorder(view_of(x), y->data, y->sB, y->sH, y->sN, es, d, perm, offset, count,
+                            inverse, (hipStream_t)stream));
+  return SPARGE_OK;
+}
+
+const char* sparge_status_str(int32_t s) {
+  switch (s) {
+    case SPARGE_OK: return "ok";
+    case SPARGE_E_NULL: return "null pointer";
+    case SPARGE_E_SHAPE: return "bad shape";
+    case SPARGE_E_DTYPE: return "bad dtype";
+    case SPARGE_E_ARG: return "bad argument";
+    case SPARGE_E_UNSUPPORTED: return "unsupported layout";
+    case SPARGE_E_WORKSPACE: return "workspace missing or too small";
+    case SPARGE_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int32_t sparge_abi_version(void) { return 1; }
+
+}  // extern "C"

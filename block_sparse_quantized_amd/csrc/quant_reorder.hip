@@ -1,0 +1,200 @@
+// int8 operands of the quantized Q K^T option and the token reorder, for gfx950.
+//
+// int8 option (SageAttention base: 8-bit quantization with outlier smoothing,
+// [topgit] "Key features"; [readme] "Avalible API").  Spec, all in IEEE fp32:
+//   K: per 64-row block, kbar_j = fp32(fp64 row sum / rows); k'' = fp32(k) - kbar_j;
+//      a = max|k''|; codes = clamp(rint(k'' * (127 / a)), -127, 127); step a / 127;
+//   Q: per 32-row group, a = max|q|, the same rounding, step a / 127.
+// Every quantity that decides an integer code is computed in the same precision
+// and order as the reference steps: fp64 sums, IEEE fp32 division, subtraction,
+// product and round-half-to-even.
+//
+// Reorder ([chapterpal] method paragraph and recommendations: Hilbert-curve token
+// order for visual inputs): gather / scatter of whole token rows by a permutation.
+#include "sparge_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace sparge {
+namespace {
+
+template <int DT>
+__device__ __forceinline__ float ldf(const void* base, int64_t idx) {
+  if constexpr (DT == kF32) return ((const float*)base)[idx];
+  else if constexpr (DT == kF16) return (float)__builtin_bit_cast(_Float16, ((const unsigned short*)base)[idx]);
+  else return __uint_as_float((unsigned int)(((const unsigned short*)base)[idx]) << 16);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ signed char quant_code(float x, float inv) {
+  float c = __builtin_rintf(x * inv);
+  c = fminf(fmaxf(c, -127.0f), 127.0f);
+  return (signed char)(int)c;
+}
+
+// One wavefront per (b, h, K block).  Lane owns D/64 channels.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void quant_k_kernel(View k, Dims d, int8_t* codes,
+                                                      int64_t crow, int64_t chead, int64_t rows_alloc,
+                                                      float* kscale, float* kbar) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= (int64_t)d.B * d.H * d.nK) return;
+  const int bh = (int)(task / d.nK), j = (int)(task % d.nK);
+  const int b = bh / d.H, h = bh % d.H;
+  const int r0 = j * kBK, n = min(kBK, d.N - r0);
+  const int64_t base = (int64_t)b * k.sB + (int64_t)h * k.sH + (int64_t)r0 * k.sN;
+  double s[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) s[c] = 0.0;
+  for (int r = 0; r < n; ++r) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s[c] = s[c] + (double)ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c);
+  }
+  float mean[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) mean[c] = (float)(s[c] / (double)n);
+  float a = 0.0f;
+  for (int r = 0; r < n; ++r) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float x = ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c) - mean[c];
+      a = fmaxf(a, fabsf(x));
+    }
+  }
+  a = wave_max_f32(a);
+  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+  int8_t* cb = codes + (int64_t)bh * chead;
+  for (int r = 0; r < kBK; ++r) {
+    const int64_t row = (int64_t)r0 + r;
+    if (row >= rows_alloc) break;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      signed char code = 0;
+      if (r < n && a > 0.0f) {
+        const float x = ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c) - mean[c];
+        code = quant_code(x, inv);
+      }
+      cb[row * crow + CPL * lane + c] = code;
+    }
+  }
+  if (lane == 0) kscale[(int64_t)bh * d.nK + j] = a > 0.0f ? a / 127.0f : 0.0f;
+  float* mb = kbar + ((int64_t)bh * d.nK + j) * D;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) mb[CPL * lane + c] = mean[c];
+}
+
+// One wavefront per (b, h, 32-row Q group).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void quant_q_kernel(View q, Dims d, int8_t* codes, float* qscale) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nG = (d.N + kQGroup - 1) / kQGroup;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= (int64_t)d.B * d.H * nG) return;
+  const int bh = (int)(task / nG), g = (int)(task % nG);
+  const int b = bh / d.H, h = bh % d.H;
+  const int r0 = g * kQGroup, n = min(kQGroup, d.N - r0);
+  const int64_t base = (int64_t)b * q.sB + (int64_t)h * q.sH + (int64_t)r0 * q.sN;
+  float a = 0.0f;
+  for (int r = 0; r < n; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      a = fmaxf(a, fabsf(ldf<DT>(q.p, base + (int64_t)r * q.sN + CPL * lane + c)));
+  a = wave_max_f32(a);
+  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+  int8_t* cb = codes + ((int64_t)bh * d.N + r0) * D;
+  for (int r = 0; r < n; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float x = ldf<DT>(q.p, base + (int64_t)r * q.sN + CPL * lane + c);
+      cb[(int64_t)r * D + CPL * lane + c] = a > 0.0f ? quant_code(x, inv) : (signed char)0;
+    }
+  if (lane == 0) qscale[(int64_t)bh * nG + g] = a > 0.0f ? a / 127.0f : 0.0f;
+}
+
+// One thread per 16-byte chunk of an output row.
+__global__ __launch_bounds__(256) void reorder_kernel(View x, void* y, int64_t ysB, int64_t ysH,
+                                                      int64_t ysN, int esize, Dims d,
+                                                      const int32_t* perm, int64_t offset,
+                                                      int64_t count, int inverse) {
+  const int chunks = d.D * esize / 16;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)d.B * d.H * d.N * chunks;
+  if (idx >= total) return;
+  const int c = (int)(idx % chunks);
+  const int64_t rowi = idx / chunks;
+  const int64_t n = rowi % d.N;
+  const int64_t bhi = rowi / d.N;
+  const int64_t b = bhi / d.H, h = bhi % d.H;
+  int64_t src = n, dst = n;
+  if (n >= offset && n < offset + count) {
+    int64_t pp = perm[n - offset];
+    pp = pp < 0 ? 0 : (pp >= count ? count - 1 : pp);
+    if (inverse) dst = offset + pp;
+    else src = offset + pp;
+  }
+  const char* xs = (const char*)x.p + (b * x.sB + h * x.sH + src * x.sN) * esize;
+  char* yd = (char*)y + (b * ysB + h * ysH + dst * ysN) * esize;
+  *(uint4*)(yd + 16 * c) = *(const uint4*)(xs + 16 * c);
+}
+
+}  // namespace
+
+hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes,
+                          int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,
+                          float* kbar, hipStream_t s) {
+  const int64_t tasks = (int64_t)d.B * d.H * d.nK;
+  const dim3 grid((unsigned)((tasks + 3) / 4));
+  const int64_t rows_alloc = codes_head_stride / codes_row_stride;
+#define SPARGE_QK(DTV, DV) \
+  quant_k_kernel<DTV, DV><<<grid, 256, 0, s>>>(k, d, codes, codes_row_stride, codes_head_stride, \
+                                               rows_alloc, kscale, kbar)
+  if (d.D == 64) {
+    if (dtype == kF32) SPARGE_QK(kF32, 64);
+    else if (dtype == kF16) SPARGE_QK(kF16, 64);
+    else SPARGE_QK(kBF16, 64);
+  } else {
+    if (dtype == kF32) SPARGE_QK(kF32, 128);
+    else if (dtype == kF16) SPARGE_QK(kF16, 128);
+    else SPARGE_QK(kBF16, 128);
+  }
+#undef SPARGE_QK
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
+                          hipStream_t s) {
+  const int nG = (d.N + kQGroup - 1) / kQGroup;
+  const int64_t tasks = (int64_t)d.B * d.H * nG;
+  const dim3 grid((unsigned)((tasks + 3) / 4));
+#define SPARGE_QQ(DTV, DV) quant_q_kernel<DTV, DV><<<grid, 256, 0, s>>>(q, d, codes, qscale)
+  if (d.D == 64) {
+    if (dtype == kF32) SPARGE_QQ(kF32, 64);
+    else if (dtype == kF16) SPARGE_QQ(kF16, 64);
+    else SPARGE_QQ(kBF16, 64);
+  } else {
+    if (dtype == kF32) SPARGE_QQ(kF32, 128);
+    else if (dtype == kF16) SPARGE_QQ(kF16, 128);
+    else SPARGE_QQ(kBF16, 128);
+  }
+#undef SPARGE_QQ
+  return hipGetLastError();
+}
+
+hipError_t launch_reorder(const View& x, void* y, int64_t ysB, int64_t ysH, int64_t ysN,
+                          int esize, const Dims& d, const int32_t* perm, int64_t offset,
+                          int64_t count, int inverse, hipStream_t s) {
+  const int chunks = d.D * esize / 16;
+  const int64_t total = (int64_t)d.B * d.H * d.N * chunks;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  reorder_kernel<<<grid, 256, 0, s>>>(x, y, ysB, ysH, ysN, esize, d, perm, offset, count, inverse);
+  return hipGetLastError();
+}
+
+}  // namespace sparge

@@ -1,0 +1,107 @@
+// Internal declarations of libsparge: kernel argument blocks, workspace layout,
+// and the host-side launch functions implemented in the .hip translation units.
+// Nothing here is part of the public ABI (include/sparge.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sparge {
+
+constexpr int kBQ = 128;  // query rows per mask block
+constexpr int kBK = 64;   // key rows per mask block
+constexpr int kQGroup = 32;  // rows per wavefront: filter group and int8 Q scale group
+
+enum ElemType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// A strided (B, H, N, D) view with unit stride along D.  Strides in elements.
+struct View {
+  const void* p;
+  int64_t sB, sH, sN;
+};
+
+struct Dims {
+  int B, H, N, D;
+  int nQ, nK;  // ceil(N/128), ceil(N/64)
+};
+
+// ---------------------------------------------------------------------------
+// Workspace: one buffer, carved into 256-byte aligned regions.
+// ---------------------------------------------------------------------------
+struct Workspace {
+  size_t qsum, qsim, ksum, ksim;   // fp64 block sums and self-similarities
+  size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
+  size_t lists, counts;            // uint16 kept-block lists (BH, nQ, nK), int32 counts
+  size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
+  size_t conv;                     // bf16 copies of fp32 q, k, v (3 x BH*N*D)
+  size_t counters;                 // 8 x uint64 stats counters
+  size_t total;
+};
+
+Workspace plan_workspace(const Dims& d, int dtype);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (return hipSuccess or the launch error).
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16 (RNE) copy of a strided view into a contiguous (B, H, N, D) buffer.
+hipError_t launch_convert_bf16(const View& x, const Dims& d, uint16_t* dst, hipStream_t s);
+
+// Per block (Q: 128 rows, K: 64 rows) channel sums in fp64 and self-similarity.
+hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dims& d,
+                              double* qsum, double* qsim, double* ksum, double* ksim,
+                              hipStream_t s);
+
+// Pooled scores s_ij = scale * qbar_i . kbar_j (fp64) for every block pair that can
+// be valid.
+hipError_t launch_pooled_scores(const double* qsum, const double* ksum, const Dims& d,
+                                int causal, double scale, double* scores, hipStream_t s);
+
+// Per block row: similarity gate, top-k selection, mask row and kept-block list.
+hipError_t launch_select(const double* scores, const double* qsim, const double* ksim,
+                         const Dims& d, int causal, double topk, double theta,
+                         uint8_t* mask_out, uint16_t* lists, int* counts,
+                         unsigned long long* counters, hipStream_t s);
+
+// User mask (or all ones when mask == nullptr) -> kept-block lists.
+hipError_t launch_compact(const uint8_t* mask, const Dims& d, uint16_t* lists, int* counts,
+                          unsigned long long* counters, hipStream_t s);
+
+// Block-smoothed int8 K: codes (BH, nK*64, D), steps (BH, nK), fp32 means (BH, nK, D).
+hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes,
+                          int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,
+                          float* kbar, hipStream_t s);
+
+// int8 Q codes with one step per 32 rows (the kernel the attention kernel mirrors).
+hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
+                          hipStream_t s);
+
+struct AttnParams {
+  View q, k, v;          // 16-bit (bf16 or fp16) views
+  void* o;               // output
+  int64_t osB, osH, osN;
+  int in_f16;            // q/k/v element type: 1 = fp16, 0 = bf16
+  int out_type;          // ElemType of the output
+  int causal, filter_on, qk_int8, pv_fp16;
+  float c;               // scale * log2(e)
+  float lam2;            // filter lambda * log2(e)
+  const uint16_t* lists;
+  const int* counts;
+  const int8_t* k8;      // int8 path: codes, (BH, nK*64, D)
+  const float* kscale;   // (BH, nK)
+  const float* kbar;     // (BH, nK, D)
+  unsigned long long* counters;  // nullable: [2] = group updates, [3] = skipped updates
+};
+
+hipError_t launch_sparse_attn(const AttnParams& p, const Dims& d, hipStream_t s);
+
+// Token reorder along N (gather or scatter by perm over [offset, offset+count)).
+hipError_t launch_reorder(const View& x, void* y, int64_t ysB, int64_t ysH, int64_t ysN,
+                          int esize, const Dims& d, const int32_t* perm, int64_t offset,
+                          int64_t count, int inverse, hipStream_t s);
+
+// Host Hilbert order (Skilling forward transform + sort).
+void hilbert_perm3d_host(int T, int Hg, int W, int32_t* perm);
+
+}  // namespace sparge

@@ -1,0 +1,373 @@
+"""GPU parity of the HIP path against the fp64 CPU oracle (needs an MI355X).
+
+Bars: the block mask is bit-exact except documented near-ties (a mismatch at
+(i, j) is excused only when s_ij lies within 1e-6 * max(1, scale * sum_c |qbar_ic
+kbar_jc|) of the row's k-th largest candidate score, or a block's similarity lies
+within 1e-6 of theta); outputs are within max-abs 2e-2 of the oracle for the
+16-bit paths and 5e-2 for the int8 Q K^T path; int8 codes and block lists are
+bit-exact.  Full-size workloads are checked on the whole mask and on sampled
+(head, block row, row group) outputs, in the launch configuration bench.py times.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import block_sparse_quantized_amd as bsq
+from block_sparse_quantized_amd import synth
+from oracle import sparge_oracle as so
+from oracle.hilbert_ref import hilbert_cell_order
+
+pytestmark = pytest.mark.gpu
+
+TOL16 = 2e-2
+TOL8 = 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def rand_qkv(B, H, N, D, dtype, dev, seed, scale=1.0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    out = [(torch.randn((B, H, N, D), generator=g) * scale).to(dtype).to(dev) for _ in range(3)]
+    return out
+
+
+def oracle_predict(q, k, params):
+    """Per-head oracle masks and infos for (B, H, N, D) tensors."""
+    qn, kn = f64(q), f64(k)
+    B, H = qn.shape[:2]
+    masks, infos = [], []
+    for b in range(B):
+        for h in range(H):
+            m, info = so.predict_mask(qn[b, h], kn[b, h], params)
+            masks.append(m)
+            infos.append(info)
+    nQ, nK = masks[0].shape
+    return np.stack(masks).reshape(B, H, nQ, nK), infos
+
+
+def unexcused_mismatches(gpu_mask, ora_mask, infos, theta=0.1):
+    """Count mask mismatches not covered by the near-tie rule."""
+    B, H, nQ, nK = ora_mask.shape
+    g = gpu_mask.reshape(B * H, nQ, nK).astype(bool)
+    o = ora_mask.reshape(B * H, nQ, nK)
+    bad, excused = 0, 0
+    for bh in range(B * H):
+        diff = np.argwhere(g[bh] != o[bh])
+        if diff.size == 0:
+            continue
+        info = infos[bh]
+        S, valid = info["scores"], info["valid"]
+        cand_all = valid & info["simk"][None, :]
+        for i, j in diff:
+            ok = abs(info["qsim"][i] - theta) <= 1e-6 or abs(info["ksim"][j] - theta) <= 1e-6
+            if not ok and cand_all[i, j] and info["kcount"][i] > 0:
+                srow = np.sort(S[i][cand_all[i]])[::-1]
+                thr = srow[info["kcount"][i] - 1]
+                mag = info["scale"] * np.abs(info["qmean"][i] * info["kmean"][j]).sum()
+                ok = abs(S[i, j] - thr) <= 1e-6 * max(1.0, mag)
+            if ok:
+                excused += 1
+            else:
+                bad += 1
+    return bad, excused
+
+
+def oracle_outputs(q, k, v, mask, causal, lam=None, scale=None):
+    qn, kn, vn = f64(q), f64(k), f64(v)
+    B, H = qn.shape[:2]
+    out = np.zeros_like(qn)
+    skipped = 0
+    for b in range(B):
+        for h in range(H):
+            o, sk = so.attend_head(qn[b, h], kn[b, h], vn[b, h], mask[b, h], causal, scale=scale,
+                                   lam=lam, return_skips=True)
+            out[b, h] = o
+            skipped += sum(len(x) for x in sk.values())
+    return out, skipped
+
+
+# ------------------------------------------------------------ block_sparse_attn
+
+@pytest.mark.parametrize("N,D,dtype", [
+    (64, 64, torch.bfloat16), (65, 128, torch.bfloat16), (127, 64, torch.float16),
+    (129, 128, torch.bfloat16), (300, 64, torch.float32), (1000, 128, torch.bfloat16),
+    (1, 64, torch.bfloat16), (513, 128, torch.float16)])
+def test_block_sparse_attn_matches_oracle(dev, N, D, dtype):
+    say(f"block_sparse_attn N={N} D={D} {dtype}")
+    B, H = 2, 3
+    q, k, v = rand_qkv(B, H, N, D, dtype, dev, seed=N + D)
+    nQ, nK = so.num_blocks(N)
+    g = torch.Generator().manual_seed(7)
+    mask = (torch.rand((B, H, nQ, nK), generator=g) < 0.45).to(torch.uint8)
+    mask[0, 0, 0] = 0                       # an empty block row -> zero output
+    if nK > 1:
+        mask[1, 2, :, -1] = 1               # ragged last K block kept
+    out = bsq.block_sparse_attn(q, k, v, mask.to(dev))
+    torch.cuda.synchronize()
+    ref, _ = oracle_outputs(q, k, v, mask.numpy().astype(bool), causal=False)
+    err = np.abs(f64(out) - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < TOL16
+    assert np.all(f64(out)[0, 0, :min(N, 128)] == 0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_sparse_dense_equals_sdpa(dev, D):
+    B, H, N = 1, 4, 777
+    q, k, v = rand_qkv(B, H, N, D, torch.bfloat16, dev, seed=3)
+    out = bsq.block_sparse_attn(q, k, v, None)
+    ref = F.scaled_dot_product_attention(q.double().cpu(), k.double().cpu(), v.double().cpu())
+    err = (out.double().cpu() - ref).abs().max().item()
+    say(f"dense D={D} err {err:.3e}")
+    assert err < TOL16
+
+
+def test_block_sparse_stats_and_lists(dev):
+    B, H, N, D = 1, 2, 1000, 64
+    q, k, v = rand_qkv(B, H, N, D, torch.bfloat16, dev, seed=5)
+    nQ, nK = so.num_blocks(N)
+    mask = (torch.rand((B, H, nQ, nK), generator=torch.Generator().manual_seed(1)) < 0.3).to(torch.uint8)
+    out, st = bsq.block_sparse_attn(q, k, v, mask.to(dev), stats=True)
+    assert st["valid_blocks"] == B * H * nQ * nK
+    assert st["kept_blocks"] == int(mask.sum())
+    groups = sum(int(mask[0, h, i].sum()) * len(range(128 * i, min(N, 128 * i + 128), 32))
+                 for h in range(H) for i in range(nQ))
+    assert st["group_updates"] == groups and st["skipped_updates"] == 0
+
+
+# ------------------------------------------------------------------ predictor
+
+@pytest.mark.parametrize("N,D,causal", [(512, 64, False), (1000, 128, True), (1000, 64, False),
+                                        (65, 64, True), (4000, 128, True)])
+def test_predict_mask_bit_exact(dev, N, D, causal):
+    wl = synth.workload("llm8k", H=4, N=N, D=D)
+    q, k, _ = synth.make_qkv(wl, device=dev)
+    for topk in (0.3, 0.5, 1.0):
+        params = so.OracleParams(topk=topk, causal=causal)
+        gm, st = bsq.sparge_predict_mask(q, k, topk, causal, stats=True)
+        om, infos = oracle_predict(q, k, params)
+        bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+        say(f"mask N={N} D={D} causal={causal} topk={topk}: unexcused {bad}, excused {exc}")
+        assert bad == 0
+        assert st["kept_blocks"] == int(gm.sum())
+        assert st["valid_blocks"] == int(sum(i["valid"].sum() for i in infos))
+
+
+def test_predict_mask_degenerate_blocks(dev):
+    B, H, N, D = 1, 2, 640, 64
+    q, k, _ = rand_qkv(B, H, N, D, torch.bfloat16, dev, seed=11)
+    q[0, 0, :128] = 0                          # zero block: similarity 0 -> forced row
+    k[0, 0, 64:128] = 0
+    k[0, 1, 128:192] = k[0, 1, 128:129]        # identical rows: similarity 1
+    q[0, 1, 256:384] = q[0, 1, 256:257]
+    for causal in (False, True):
+        gm = bsq.sparge_predict_mask(q, k, 0.4, causal)
+        om, infos = oracle_predict(q, k, so.OracleParams(topk=0.4, causal=causal))
+        bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+        assert bad == 0
+
+
+# ------------------------------------------------------------- sparge_topk_attn
+
+def test_tiny_workload_end_to_end(dev):
+    wl = synth.WORKLOADS["tiny"]
+    q, k, v = synth.make_qkv(wl, device=dev)
+    out, gm = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=False, return_mask=True)
+    om, infos = oracle_predict(q, k, so.OracleParams(topk=wl.topk, causal=wl.causal))
+    bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+    assert bad == 0 and exc == 0
+    ref, _ = oracle_outputs(q, k, v, gm.cpu().numpy().astype(bool), wl.causal)
+    err = np.abs(f64(out) - ref).max()
+    say(f"tiny workload err {err:.3e}, density {gm.float().mean().item():.3f}")
+    assert err < TOL16
+
+
+@pytest.mark.parametrize("N,D,causal", [(700, 64, True), (1000, 128, False), (129, 128, True)])
+def test_topk_attn_topk1_filter_off_is_dense(dev, N, D, causal):
+    q, k, v = rand_qkv(1, 2, N, D, torch.bfloat16, dev, seed=N)
+    out = bsq.sparge_topk_attn(q, k, v, 1.0, causal, filter_on=False)
+    ref = F.scaled_dot_product_attention(q.double().cpu(), k.double().cpu(), v.double().cpu(),
+                                         is_causal=causal)
+    assert (out.double().cpu() - ref).abs().max().item() < TOL16
+
+
+def _filter_inputs(dev, N=1024, D=64, H=2):
+    g = torch.Generator().manual_seed(2)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm() * 8.0
+    q = torch.randn((1, H, N, D), generator=g) + u
+    k = torch.randn((1, H, N, D), generator=g) * 0.5
+    k[:, :, :64] += 3 * u      # block 0: logits ~24 above the rest for every row (margin >> |lambda|)
+    v = torch.randn((1, H, N, D), generator=g)
+    return [t.to(torch.bfloat16).to(dev) for t in (q, k, v)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_filter_skips_match_oracle(dev, causal):
+    q, k, v = _filter_inputs(dev)
+    # topk attention with topk=1 keeps every valid block, so the filter alone decides
+    out, gm, st = bsq.sparge_topk_attn(q, k, v, 1.0, causal, filter_on=True, return_mask=True,
+                                        stats=True)
+    ref, skipped = oracle_outputs(q, k, v, gm.cpu().numpy().astype(bool), causal, lam=-10.0)
+    err = np.abs(f64(out) - ref).max()
+    say(f"filter causal={causal}: skipped gpu {st['skipped_updates']} oracle {skipped}, err {err:.3e}")
+    assert skipped > 0
+    assert st["skipped_updates"] == skipped
+    assert err < TOL16
+
+
+# -------------------------------------------------------------------- int8 path
+
+@pytest.mark.parametrize("dtype,N,D", [(torch.bfloat16, 1000, 128), (torch.float32, 333, 64),
+                                       (torch.float16, 64, 64)])
+def test_int8_codes_bit_exact(dev, dtype, N, D):
+    wl = synth.workload("llm8k", H=3, N=N, D=D, dtype=dtype)
+    q, k, _ = synth.make_qkv(wl, device=dev)
+    q[0, 1, :32] = 0                                   # an all-zero Q group
+    r = bsq.sparge_quantize_qk(q, k)
+    qn = q.float().cpu().numpy()
+    kn = k.float().cpu().numpy()
+    for h in range(3):
+        qc, qd, kc, kd, kbar = so.int8_qk_inputs(qn[0, h], kn[0, h], 32)
+        assert np.array_equal(r["q_codes"][0, h].cpu().numpy(), qc)
+        assert np.array_equal(r["q_scales"][0, h].cpu().numpy(), qd)
+        assert np.array_equal(r["k_means"][0, h].cpu().numpy(), kbar)
+        assert np.array_equal(r["k_scales"][0, h].cpu().numpy(), kd)
+        assert np.array_equal(r["k_codes"][0, h].cpu().numpy(), kc)
+
+
+@pytest.mark.parametrize("N,D,causal,pv16", [(2000, 128, True, True), (1500, 64, False, False),
+                                             (300, 128, False, True)])
+def test_int8_attention(dev, N, D, causal, pv16):
+    wl = synth.workload("llm8k", H=2, N=N, D=D)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, causal, qk_int8=True, pv_fp16=pv16,
+                                   filter_on=False, return_mask=True)
+    mask = gm.cpu().numpy().astype(bool)
+    ref, _ = oracle_outputs(q, k, v, mask, causal)
+    err = np.abs(f64(out) - ref).max()
+    qn, kn, vn = f64(q), f64(k), f64(v)
+    sim_err = 0.0
+    for h in range(2):
+        o8 = so.attend_head_int8_sim(qn[0, h].astype(np.float32), kn[0, h].astype(np.float32),
+                                     vn[0, h], mask[0, h], causal,
+                                     pv_round="fp16" if pv16 else "bf16")
+        sim_err = max(sim_err, np.abs(f64(out)[0, h] - o8).max())
+    say(f"int8 N={N} D={D}: err vs fp64 {err:.3e}, vs int8 simulation {sim_err:.3e}")
+    assert err < TOL8
+    assert sim_err < TOL16
+
+
+# -------------------------------------------------------------- Hilbert reorder
+
+def test_reorder_gather_scatter(dev):
+    T, Hg, W, text = 3, 8, 10, 17
+    N = text + T * Hg * W
+    x = torch.randn((2, 3, N, 64), device=dev).to(torch.bfloat16)
+    perm = bsq.sparge_hilbert_perm3d(T, Hg, W)
+    assert np.array_equal(perm.numpy().astype(np.int64), hilbert_cell_order(T, Hg, W))
+    pd = perm.to(dev)
+    y = bsq.sparge_reorder(x, pd, text, T * Hg * W)
+    full = torch.cat([torch.arange(text), text + perm.long()]).to(dev)
+    assert torch.equal(y, x[:, :, full])
+    back = bsq.sparge_reorder(y, pd, text, T * Hg * W, inverse=True)
+    assert torch.equal(back, x)
+
+
+def test_video_pipeline_small(dev):
+    wl = synth.workload("video", B=1, H=2, N=10 + 3 * 16 * 16, text=10, grid=(3, 16, 16))
+    q, k, v = synth.make_qkv(wl, device=dev)
+    cells = 3 * 16 * 16
+    perm = bsq.sparge_hilbert_perm3d(3, 16, 16).to(dev)
+    qr, kr, vr = (bsq.sparge_reorder(t, perm, 10, cells) for t in (q, k, v))
+    o_r, gm = bsq.sparge_topk_attn(qr, kr, vr, 0.3, False, return_mask=True)
+    out = bsq.sparge_reorder(o_r, perm, 10, cells, inverse=True)
+    fullp = np.concatenate([np.arange(10), 10 + hilbert_cell_order(3, 16, 16)])
+    qn, kn, vn = f64(q)[:, :, fullp], f64(k)[:, :, fullp], f64(v)[:, :, fullp]
+    om = np.zeros(gm.shape, dtype=bool)
+    for h in range(2):
+        m, info = so.predict_mask(qn[0, h], kn[0, h], so.OracleParams(topk=0.3))
+        om[0, h] = m
+        o, _ = so.attend_head(qn[0, h], kn[0, h], vn[0, h], m, False, lam=-10.0, return_skips=True)
+        back = np.empty_like(o)
+        back[fullp] = o
+        err = np.abs(f64(out)[0, h] - back).max()
+        say(f"video small head {h}: err {err:.3e}")
+        assert err < TOL16
+    assert np.array_equal(gm.cpu().numpy().astype(bool), om)
+
+
+# ------------------------------------------------------ full-size workloads
+
+def run_workload(wl, q, k, v, mask=None, stats=False):
+    """The exact call sequence bench.py times for a workload."""
+    if wl.api == "block_sparse":
+        return bsq.block_sparse_attn(q, k, v, mask, filter_on=wl.filter_on, qk_int8=wl.qk_int8,
+                                     pv_fp16=wl.pv_fp16, stats=stats)
+    return bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
+                                qk_int8=wl.qk_int8, pv_fp16=wl.pv_fp16, return_mask=True,
+                                stats=stats)
+
+
+def sample_groups(B, H, N, n, seed, causal):
+    r = np.random.default_rng(seed)
+    nQ = (N + 127) // 128
+    picks = [(0, 0, nQ - 1, (N - 1 - 128 * (nQ - 1)) // 32)]   # the ragged last group
+    while len(picks) < n:
+        b, h = int(r.integers(B)), int(r.integers(H))
+        i = int(r.integers(nQ)) if not causal or r.random() < 0.5 else nQ - 1 - int(r.integers(4))
+        gmax = (min(N, 128 * i + 128) - 128 * i + 31) // 32
+        picks.append((b, h, i, int(r.integers(gmax))))
+    return picks
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llm8k", "image", "video", "llm128k"])
+def test_full_workload(dev, name):
+    wl = synth.WORKLOADS[name]
+    say(f"full workload {name}: generating on {dev}")
+    q, k, v = synth.make_qkv(wl, device=dev)
+    mask_in = synth.make_block_mask(wl, device=dev) if wl.api == "block_sparse" else None
+    if wl.hilbert:
+        cells = int(np.prod(wl.grid))
+        perm = bsq.sparge_hilbert_perm3d(*wl.grid).to(dev)
+        q, k, v = (bsq.sparge_reorder(t, perm, wl.text, cells) for t in (q, k, v))
+    res = run_workload(wl, q, k, v, mask_in, stats=True)
+    torch.cuda.synchronize()
+    if wl.api == "block_sparse":
+        out, st = res
+        mask = mask_in.cpu().numpy().astype(bool)
+    else:
+        out, gm, st = res
+        mask = gm.cpu().numpy().astype(bool)
+        om, infos = oracle_predict(q, k, so.OracleParams(topk=wl.topk, causal=wl.causal))
+        bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+        say(f"  mask: unexcused {bad}, excused {exc}, density {mask.mean():.3f}")
+        assert bad == 0
+    say(f"  stats {st}")
+    assert st["kept_blocks"] == int(mask.sum())
+    lam = -10.0 if wl.filter_on else None
+    tol = TOL8 if wl.qk_int8 else TOL16
+    B, H, N, D = q.shape
+    worst = 0.0
+    for (b, h, i, g) in sample_groups(B, H, N, 8, seed=len(name), causal=wl.causal):
+        qn, kn, vn = f64(q[b, h]), f64(k[b, h]), f64(v[b, h])
+        ref = so.attend_rows(qn, kn, vn, mask[b, h], [(i, g)], wl.causal, lam=lam)[(i, g)]
+        t0 = 128 * i + 32 * g
+        got = f64(out[b, h, t0:t0 + ref.shape[0]])
+        err = np.abs(got - ref).max()
+        worst = max(worst, err)
+        say(f"  sample b={b} h={h} i={i} g={g}: err {err:.3e}")
+    assert worst < tol
