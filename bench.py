@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the SpargeAttn hot path on MI355X; prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-extras]
+
+A step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM:
+  llm128k (default; B=1 H=32 N=131072 D=128, causal, topk=0.5): stage-1 predictor
+      (block stats, pooled scores, top-k select), block-smoothed int8 K
+      quantization, stage-2 sparse attention (int8 Q K^T, fp16 P.V, filter on);
+  llm8k: the same recipe at N=8192 with 16-bit Q K^T and P.V;
+  video: Hilbert gather of Q/K/V, the same path (topk=0.3, non-causal, D=64),
+      scatter of O back to token order;
+  image: block_sparse_attn under a seeded Bernoulli(0.3) block mask.
+`value` is dense-equivalent TOPS of the whole step: 4*B*H*N^2*D (halved when
+causal) per step / step time.  `roofline` covers the attention kernel alone,
+timed with HIP events recorded around its launch on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv TOPS & latency of sparse attn at N=8K..128K, topk=0.5; MFMA util"
+PEAK_BF16 = 2.5e15      # dense bf16/fp16 MFMA, FLOP/s (MI355X published)
+PEAK_INT8 = 5.0e15      # dense int8 MFMA, OP/s
+BK, BQ, G = 64, 128, 32
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime instance torch and libsparge share."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime)
+        maps = open("/proc/self/maps").read()
+        paths = sorted(set(re.findall(r"(\S*libamdhip64\.so\S*)", maps)))
+        self.hip = ctypes.CDLL(paths[0] if paths else "libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+def dense_equiv_ops(B, H, N, D, causal):
+    ops = 4.0 * B * H * N * N * D
+    return ops / 2 if causal else ops
+
+
+class Path:
+    """The hot path of one workload with preallocated outputs and workspace."""
+
+    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None):
+        import torch
+
+        import block_sparse_quantized_amd as bsq
+        from block_sparse_quantized_amd import synth
+        self.bsq, self.wl, self.dev = bsq, wl, dev
+        self.qk_int8 = wl.qk_int8 if qk_int8 is None else qk_int8
+        self.pv_fp16 = wl.pv_fp16 if pv_fp16 is None else pv_fp16
+        t0 = time.time()
+        if inputs is None:
+            self.q, self.k, self.v = synth.make_qkv(wl, device=dev)
+            self.mask = synth.make_block_mask(wl, device=dev) if wl.api == "block_sparse" else None
+            torch.cuda.synchronize()
+            log(f"[bench] generated {wl.name} inputs on {dev} in {time.time() - t0:.1f}s")
+        else:
+            self.q, self.k, self.v, self.mask = inputs
+        self.out = torch.empty_like(self.q)
+        self.ws = torch.empty(bsq.sparge_workspace_bytes(*self.q.shape, self.q.dtype),
+                              dtype=torch.uint8, device=dev)
+        if wl.hilbert:
+            self.cells = 1
+            for s in wl.grid:
+                self.cells *= s
+            self.perm = bsq.sparge_hilbert_perm3d(*wl.grid).to(dev)
+            self.qr, self.kr, self.vr, self.orr = (torch.empty_like(self.q) for _ in range(4))
+
+    def step(self, prof=None, stats=False):
+        bsq, wl = self.bsq, self.wl
+        q, k, v, out = self.q, self.k, self.v, self.out
+        if wl.hilbert:
+            bsq.sparge_reorder(q, self.perm, wl.text, self.cells, out=self.qr)
+            bsq.sparge_reorder(k, self.perm, wl.text, self.cells, out=self.kr)
+            bsq.sparge_reorder(v, self.perm, wl.text, self.cells, out=self.vr)
+            q, k, v, out = self.qr, self.kr, self.vr, self.orr
+        if wl.api == "block_sparse":
+            r = bsq.block_sparse_attn(q, k, v, self.mask, filter_on=wl.filter_on,
+                                      qk_int8=self.qk_int8, pv_fp16=self.pv_fp16, stats=stats,
+                                      out=out, workspace=self.ws, prof=prof)
+        else:
+            r = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
+                                     qk_int8=self.qk_int8, pv_fp16=self.pv_fp16, stats=stats,
+                                     out=out, workspace=self.ws, prof=prof)
+        if wl.hilbert:
+            bsq.sparge_reorder(self.orr, self.perm, wl.text, self.cells, inverse=True, out=self.out)
+        return r
+
+
+def time_path(path, ev, steps, warmup):
+    """Whole-step wall time (synchronised) and per-launch attention-kernel time."""
+    import torch
+    for _ in range(warmup):
+        path.step()
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        path.step(prof=evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn = [ev.elapsed_ms(e[1], e[2]) for e in evs]
+    pre = [ev.elapsed_ms(e[0], e[1]) for e in evs]
+    return (t1 - t0) * 1e3 / steps, sum(attn) / steps, sum(pre) / steps
+
+
+def algorithmic_work(stats, D, qk_int8):
+    """(QK ops, PV flops) the attention kernel executes per launch on computed tiles.
+
+    Per visited (32-row group, kept 64-key block): Q K^T 2*32*64*D; P.V 2*32*64*D
+    unless the filter dropped the update."""
+    per = 2.0 * G * BK * D
+    qk = stats["group_updates"] * per
+    pv = (stats["group_updates"] - stats["skipped_updates"]) * per
+    return qk, pv
+
+
+def roofline(stats, D, qk_int8, attn_ms, traffic):
+    qk, pv = algorithmic_work(stats, D, qk_int8)
+    t = attn_ms * 1e-3
+    if qk_int8:
+        # mixed roofline: the int8 Q K^T at the int8 peak plus the 16-bit P.V at the
+        # bf16/fp16 peak; the effective peak is the work over that minimum time
+        peak = (qk + pv) / (qk / PEAK_INT8 + pv / PEAK_BF16)
+    else:
+        peak = PEAK_BF16
+    achieved = (qk + pv) / t
+    return {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+            "frac_of_bf16_peak": round(achieved / PEAK_BF16, 4),
+            "kernel": "sparse_attn_kernel", "ms_per_launch": round(attn_ms, 4),
+            "work_per_launch": {"qk_ops": qk, "pv_flops": pv}}
+
+
+def committed_traffic(wl_name, kernel_src):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"sparse_attn_{wl_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, q, k, v, budget_s=20.0):
+    """The CPU oracle (fp64 numpy) timed on a bounded sample of the workload."""
+    import numpy as np
+
+    from oracle import sparge_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    B, H, N, D = q.shape
+    qn = q[0, 0].double().cpu().numpy()
+    kn = k[0, 0].double().cpu().numpy()
+    vn = v[0, 0].double().cpu().numpy()
+    t0 = time.perf_counter()
+    if wl.api == "block_sparse":
+        from block_sparse_quantized_amd import synth
+        mask = synth.make_block_mask(wl, device="cpu")[0, 0].numpy().astype(bool)
+        t_pred = 0.0
+    else:
+        mask, _ = so.predict_mask(qn, kn, so.OracleParams(topk=wl.topk, causal=wl.causal))
+        t_pred = time.perf_counter() - t0
+    nQ = mask.shape[0]
+    lam = -10.0 if wl.filter_on else None
+    # block rows visited in a fixed spread (longest first), until the budget is spent
+    order = []
+    for stride in (max(1, nQ // 8), max(1, nQ // 64), 1):
+        order += [i for i in range(nQ - 1, -1, -stride) if i not in order]
+    done_rows, dense_ops, t_attn = 0, 0.0, 0.0
+    groups = []
+    for i in order:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        for g in range(4):
+            r0 = BQ * i + G * g
+            if r0 >= N:
+                continue
+            r1 = min(N, r0 + G, BQ * i + BQ)
+            t1 = time.perf_counter()
+            so.attend_rows(qn, kn, vn, mask, [(i, g)], wl.causal, lam=lam)
+            t_attn += time.perf_counter() - t1
+            rows = np.arange(r0, r1)
+            keys = (rows + 1) if wl.causal else np.full(rows.size, N)
+            dense_ops += float(4.0 * D * keys.sum())
+            done_rows += r1 - r0
+            groups.append((i, g))
+    t = t_attn + t_pred * done_rows / N
+    return {"value": round(dense_ops / t / 1e12, 8), "unit": "TOPS (dense-equivalent)",
+            "cores": cores, "kind": "oracle",
+            "sample": (f"head (0,0) of {wl.name}: full stage-1 oracle predictor ({t_pred:.2f}s, "
+                       f"pro-rated by rows) + stage-2 fp64 oracle attention"
+                       f"{' with the filter' if lam is not None else ''} for {len(groups)} "
+                       f"32-row groups ({done_rows} rows in {len(set(i for i, _ in groups))} block rows, "
+                       f"spread over the sequence, longest first); "
+                       f"value = dense-equivalent ops of those rows / time ({t:.2f}s)")}
+
+
+def sdpa_baseline(q, k, v, causal, steps=3):
+    """torch SDPA (flash / memory-efficient only) in bf16 at the same shape."""
+    import torch
+    import torch.nn.functional as F
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        qb, kb, vb = (t.to(torch.bfloat16) for t in (q, k, v))
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            F.scaled_dot_product_attention(qb, kb, vb, is_causal=causal)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                F.scaled_dot_product_attention(qb, kb, vb, is_causal=causal)
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+    except Exception as e:  # no fused backend at this shape
+        log(f"[bench] torch SDPA baseline unavailable: {e}")
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llm128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path shards over (batch, head) with no "
+              f"communication and multi-GPU runs are not part of this build; got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_quantized_amd import synth
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    ev = HipEvents()
+    log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D} steps={args.steps} "
+        f"warmup={args.warmup}")
+
+    path = Path(wl, dev)
+    _, stats = path.step(stats=True)
+    torch.cuda.synchronize()
+    ms_step, ms_attn, ms_pre = time_path(path, ev, args.steps, args.warmup)
+    log(f"[bench] step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, before-attention {ms_pre:.3f} ms")
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    dense = dense_equiv_ops(B, H, N, D, wl.causal)
+    value = dense / (ms_step * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "block_sparse_quantized_amd", "csrc", "attn.hip")
+    roof = roofline(stats, D, path.qk_int8, ms_attn, committed_traffic(wl.name, kernel_src))
+
+    extras = {}
+    if not args.no_extras:
+        if path.qk_int8 or path.pv_fp16:
+            p16 = Path(wl, dev, qk_int8=False, pv_fp16=False,
+                       inputs=(path.q, path.k, path.v, path.mask))
+            _, st16 = p16.step(stats=True)
+            s16, a16, _ = time_path(p16, ev, max(3, args.steps // 2), 1)
+            extras["bf16_variant"] = {"ms_per_step": round(s16, 3),
+                                      "tops_dense_equiv": round(dense / (s16 * 1e-3) / 1e12, 2),
+                                      "roofline": roofline(st16, D, False, a16, None)}
+            del p16
+        if wl.api != "block_sparse" and not wl.hilbert:
+            pd = Path(synth.workload(wl.name, topk=1.0, filter_on=False), dev, qk_int8=False,
+                      pv_fp16=False, inputs=(path.q, path.k, path.v, path.mask))
+            sd, _, _ = time_path(pd, ev, 3, 1)
+            extras["dense_ours_bf16"] = {"ms_per_step": round(sd, 3),
+                                         "tops_dense_equiv": round(dense / (sd * 1e-3) / 1e12, 2)}
+            del pd
+        ms_sdpa = sdpa_baseline(path.q, path.k, path.v, wl.causal)
+        if ms_sdpa is not None:
+            extras["dense_torch_sdpa_bf16"] = {"ms_per_step": round(ms_sdpa, 3),
+                                              "tops_dense_equiv": round(dense / (ms_sdpa * 1e-3) / 1e12, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(wl, path.q, path.k, path.v)
+        log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
+
+    density = stats["kept_blocks"] / max(1, stats["valid_blocks"])
+    dtype = ("i8-qk/f16-pv" if path.pv_fp16 else "i8-qk/bf16-pv") if path.qk_int8 else \
+        ("f16-pv/bf16-qk" if path.pv_fp16 else "bf16")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded torch generators on the GPU; see block_sparse_quantized_amd/synth.py)",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
+                   "topk": wl.topk if wl.api != "block_sparse" else None, "api": wl.api,
+                   "filter_on": wl.filter_on, "qk_int8": path.qk_int8, "pv_fp16": path.pv_fp16,
+                   "hilbert": wl.hilbert},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "latency_ms": {"step": round(ms_step, 4), "attention_kernel": round(ms_attn, 4),
+                       "before_attention": round(ms_pre, 4)},
+        "sparsity": {"kept_block_density": round(density, 4),
+                     "filter_skip_frac": round(stats["skipped_updates"] / max(1, stats["group_updates"]), 5),
+                     **stats},
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
