@@ -28,7 +28,7 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
   w.kscale = take(BH * d.nK * sizeof(float));
   w.kbar = take(BH * d.nK * d.D * sizeof(float));
-  w.conv = take(dtype == kF32 ? 3 * BH * (size_t)d.N * d.D * sizeof(uint16_t) : 0);
+  w.conv = take(3 * BH * (size_t)d.N * d.D * sizeof(uint16_t));
   w.counters = take(8 * sizeof(unsigned long long));
   w.total = off;
   return w;
@@ -130,7 +130,9 @@ sparge_status end_stats(Ctx& c, const sparge_opts* o) {
   return SPARGE_OK;
 }
 
-// The attention operands: 16-bit views (fp32 inputs are rounded into the workspace).
+// The attention operands: Q and K as 16-bit views (fp32 inputs rounded to bf16
+// into the workspace), V in the P.V type (converted into the workspace when it
+// differs from the input's type, once per call rather than once per block).
 struct Operands {
   View q, k, v;
   int in_f16;
@@ -138,25 +140,32 @@ struct Operands {
 };
 
 sparge_status prepare_operands(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
-                               const sparge_tensor* v, Operands& op) {
+                               const sparge_tensor* v, int pv_fp16, Operands& op) {
+  const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
+  uint16_t* base = c.at<uint16_t>(c.w.conv);
+  const View packed_strides{nullptr, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D,
+                            (int64_t)c.d.D};
+  auto converted = [&](uint16_t* o) { View r = packed_strides; r.p = o; return r; };
   if (q->dtype == SPARGE_F32) {
-    const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
-    uint16_t* base = c.at<uint16_t>(c.w.conv);
-    const sparge_tensor* src[3] = {q, k, v};
-    View* dst[3] = {&op.q, &op.k, &op.v};
-    for (int x = 0; x < 3; ++x) {
-      uint16_t* o = base + x * one;
-      SPARGE_TRY(launch_convert_bf16(view_of(src[x]), c.d, o, c.s));
-      *dst[x] = View{o, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
-    }
+    SPARGE_TRY(launch_convert16(view_of(q), kF32, c.d, base, 0, c.s));
+    SPARGE_TRY(launch_convert16(view_of(k), kF32, c.d, base + one, 0, c.s));
+    op.q = converted(base);
+    op.k = converted(base + one);
     op.in_f16 = 0;
     op.dtype16 = kBF16;
   } else {
     op.q = view_of(q);
     op.k = view_of(k);
-    op.v = view_of(v);
     op.in_f16 = q->dtype == SPARGE_F16;
     op.dtype16 = q->dtype;
+  }
+  const int v_f16 = pv_fp16 ? 1 : op.in_f16;
+  const int v_native = (v->dtype == SPARGE_F16 && v_f16) || (v->dtype == SPARGE_BF16 && !v_f16);
+  if (v_native) {
+    op.v = view_of(v);
+  } else {
+    SPARGE_TRY(launch_convert16(view_of(v), v->dtype, c.d, base + 2 * one, v_f16, c.s));
+    op.v = converted(base + 2 * one);
   }
   return SPARGE_OK;
 }
@@ -269,7 +278,7 @@ sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   Operands op;
-  if ((st = prepare_operands(c, q, k, v, op)) != SPARGE_OK) return st;
+  if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) return st;
   if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
   if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0)) != SPARGE_OK) return st;
   return end_stats(c, &o);
@@ -293,7 +302,7 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   Operands op;
-  if ((st = prepare_operands(c, q, k, v, op)) != SPARGE_OK) return st;
+  if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) return st;
   SPARGE_TRY(launch_compact(mask_id, c.d, c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts),
                             c.counters, c.s));
   if ((st = run_attention(c, op, out, o, 0, o.filter_on != 0)) != SPARGE_OK) return st;

@@ -32,6 +32,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 
@@ -68,6 +69,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 // {4h..4h+3, 8+4h..8+4h+3} of the group as its 8 consecutive k slots.
 __device__ __forceinline__ int vpos4(int g) { return (g == 1) ? 8 : (g == 2 ? 4 : 4 * g); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded (to nearest even) into one packed 16-bit pair.
+template <bool F16>
+__device__ __forceinline__ unsigned int pack2(float a, float b) {
+  if constexpr (F16) return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, f16x2));
+  else return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// acc + (lo + hi) of a packed 16-bit pair, accumulated in fp32.
+template <bool F16>
+__device__ __forceinline__ float add_pair(unsigned int pr, float acc) {
+  if constexpr (F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
+                                           (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Key offset, inside a 64-key block, of register r of key tile kt for lane half 0
+// (half 1 adds 4): the 32x32 MFMA result layout.
+__device__ __forceinline__ constexpr int key_off(int kt, int r) { return 32 * kt + (r >> 2) * 8 + (r & 3); }
+
+// Reference-max slack (log2 units): exponentials are taken against a reference
+// max that moves only when a row's running max exceeds it by more than this, so
+// O and l are rescaled rarely; P then stays below 2^8.
+constexpr float kTau = 8.0f;
+
 template <int D, bool IN_F16, bool PV_F16, bool QK8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims d) {
   constexpr int KS16 = D / 16;                 // k-steps of the 16-bit Q K^T
@@ -98,11 +131,13 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const int wrow0 = i * 128 + w * 32;
   const int t = wrow0 + ql;
   const bool row_ok = t < N;
+  // keys s < lim are visible to this lane's query row
+  const int lim = row_ok ? (p.causal ? min(N, t + 1) : N) : 0;
 
   const unsigned short* Qp = (const unsigned short*)p.q.p + b * p.q.sB + h * p.q.sH;
-  const unsigned short* Kp = (const unsigned short*)p.k.p + b * p.k.sB + h * p.k.sH;
-  const unsigned short* Vp = (const unsigned short*)p.v.p + b * p.v.sB + h * p.v.sH;
-  const int8_t* K8p = QK8 ? p.k8 + (int64_t)bh * d.nK * 64 * D : nullptr;
+  const char* Kb = QK8 ? (const char*)(p.k8 + (int64_t)bh * d.nK * 64 * D)
+                       : (const char*)((const unsigned short*)p.k.p + b * p.k.sB + h * p.k.sH);
+  const char* Vb = (const char*)((const unsigned short*)p.v.p + b * p.v.sB + h * p.v.sH);
 
   // Q fragments in the B-operand layout: lane (hf, ql) holds Q[t][16s + 8hf .. +7].
   u16x8 qf[KS16];
@@ -157,32 +192,51 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x16)(0.0f);
-  float m_run = kNegInf, l_part = 0.0f;
+  float m_true = kNegInf;   // running row max of the visited blocks (filter)
+  float m_ref = kNegInf;    // reference max of the exponentials
+  float m_use = 0.0f;       // m_ref, or 0 while it is -inf
+  float l_acc = 0.0f;       // this lane's partial row sum (its half of the keys)
   unsigned int n_skip = 0;
+
+  // per-thread staging addresses (bytes from the head base), fixed over the loop
+  int koff[KCH], krow[KCH];
+#pragma unroll
+  for (int u = 0; u < KCH; ++u) {
+    const int c = tid + 256 * u;
+    krow[u] = c / KCPR;
+    koff[u] = QK8 ? krow[u] * D + 16 * (c % KCPR) : (krow[u] * (int)p.k.sN + 8 * (c % KCPR)) * 2;
+  }
+  // V staging task of this thread: 4-key run g4 (16 per block) x 8-column chunk dc.
+  // Sixteen consecutive lanes take the sixteen runs of one chunk, so each
+  // transposed LDS store instruction covers whole 128-byte rows (no bank conflicts).
+  const bool vtask = (VTASK == 256) || (tid < VTASK);
+  const int g4 = tid & 15, dc = tid >> 4;
+  const int voff = (4 * g4 * (int)p.v.sN + 8 * dc) * 2;
+  const int vrow = (int)p.v.sN * 2;
+  const int64_t kblk = QK8 ? (int64_t)64 * D : (int64_t)64 * p.k.sN * 2;
+  const int64_t vblk = (int64_t)64 * p.v.sN * 2;
 
   u16x8 kreg[KCH];
   u16x8 vreg[4];
 
   auto load_tile = [&](int j) {
+    const char* kb = Kb + j * kblk;
+    const char* vb = Vb + j * vblk;
+    if (QK8 || 64 * j + 64 <= N) {
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + 256 * u;
-      const int row = c / KCPR, col = c % KCPR;
-      const int key = 64 * j + row;
-      if constexpr (QK8) {
-        kreg[u] = *(const u16x8*)(K8p + (int64_t)key * D + 16 * col);
-      } else {
-        if (key < N) kreg[u] = *(const u16x8*)(Kp + (int64_t)key * p.k.sN + 8 * col);
-        else kreg[u] = (u16x8)(0);
+      for (int u = 0; u < KCH; ++u) kreg[u] = *(const u16x8*)(kb + koff[u]);
+      if (vtask) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[r] = *(const u16x8*)(vb + voff + r * vrow);
       }
-    }
-    if (VTASK == 256 || tid < VTASK) {
-      const int g4 = tid / (D / 8), dc = tid % (D / 8);
+    } else {  // ragged last block: rows past N read as zeros
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 64 * j + 4 * g4 + r;
-        if (key < N) vreg[r] = *(const u16x8*)(Vp + (int64_t)key * p.v.sN + 8 * dc);
-        else vreg[r] = (u16x8)(0);
+      for (int u = 0; u < KCH; ++u)
+        kreg[u] = (64 * j + krow[u] < N) ? *(const u16x8*)(kb + koff[u]) : (u16x8)(0);
+      if (vtask) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vreg[r] = (64 * j + 4 * g4 + r < N) ? *(const u16x8*)(vb + voff + r * vrow) : (u16x8)(0);
       }
     }
   };
@@ -191,21 +245,13 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = tid + 256 * u;
-      const int row = c / KCPR, col = c % KCPR;
-      *(u16x8*)(&Ks[buf][row * KROWB + 16 * col]) = kreg[u];
+      *(u16x8*)(&Ks[buf][(c / KCPR) * KROWB + 16 * (c % KCPR)]) = kreg[u];
     }
-    if (VTASK == 256 || tid < VTASK) {
-      const int g4 = tid / (D / 8), dc = tid % (D / 8);
+    if (vtask) {
       const int pos = 16 * (g4 >> 2) + vpos4(g4 & 3);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        u16x4 v4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const unsigned short raw = vreg[r][e];
-          if constexpr (IN_F16 == PV_F16) v4[r] = raw;
-          else v4[r] = f32_to_u16<PV_F16>(u16_to_f32(raw, IN_F16));
-        }
+        const u16x4 v4 = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
         *(u16x4*)(&Vs[buf][(8 * dc + e) * VSTR + pos]) = v4;
       }
     }
@@ -226,7 +272,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       unsigned short* kbl = kbh + 32 * KBSTR;                // [32][KBSTR] lo
       float* cw = (float*)Aux + w * 32 * 33;                 // per wave [32][33]
       if ((it & 31) == 0) {
-        // kbar of the next 32 kept blocks as bf16 hi + lo, for q . kbar by MFMA
+        // kbar of the next 32 kept blocks as hi + lo in the input's 16-bit type,
+        // so that q . kbar runs on the MFMA at near-fp32 accuracy
         for (int e = tid; e < 32 * (D / 4); e += 256) {
           const int pr = e / (D / 4), c4 = (e % (D / 4)) * 4;
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -235,7 +282,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            // kbar = hi + lo in the input's 16-bit type (exact to ~2^-17 relative)
             const unsigned short hi = f32_to_u16<IN_F16>(vv[q4]);
             const unsigned short lo = f32_to_u16<IN_F16>(vv[q4] - u16_to_f32(hi, IN_F16));
             kbh[pr * KBSTR + c4 + q4] = hi;
@@ -258,91 +304,105 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         __syncthreads();
       }
       bias = p.c * cw[(it & 31) * 33 + ql];
-      sc = p.c * dq * p.kscale[(int64_t)bh * d.nK + j];
+      // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
+      // that masked (-inf) scores stay -inf
+      sc = fmaxf(p.c * dq * p.kscale[(int64_t)bh * d.nK + j], 1e-30f);
     }
 
-    // logits (log2 units) of this lane's query against the block's 64 keys:
-    // lg[kt][r] is key 32kt + (r/4)*8 + 4hf + r%4
-    float lg[2][16];
+    // raw scores of this lane's query against the block's 64 keys:
+    // sacc[kt][r] is key 64j + 4hf + key_off(kt, r)
+    f32x16 sacc[2];
     if constexpr (!QK8) {
+      sacc[0] = (f32x16)(0.0f);
+      sacc[1] = (f32x16)(0.0f);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc = (f32x16)(0.0f);
+      for (int s = 0; s < KS16; ++s)
 #pragma unroll
-        for (int s = 0; s < KS16; ++s) {
+        for (int kt = 0; kt < 2; ++kt) {
           const u16x8 kf = *(const u16x8*)(&Ks[buf][(32 * kt + ql) * KROWB + 32 * s + 16 * hf]);
-          sacc = mma16<IN_F16>(kf, qf[s], sacc);
+          sacc[kt] = mma16<IN_F16>(kf, qf[s], sacc[kt]);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lg[kt][r] = sacc[r] * p.c;
-      }
     } else {
+      i32x16 iacc[2] = {(i32x16)(0), (i32x16)(0)};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        i32x16 iacc = (i32x16)(0);
+      for (int s = 0; s < KS8; ++s)
 #pragma unroll
-        for (int s = 0; s < KS8; ++s) {
+        for (int kt = 0; kt < 2; ++kt) {
           const i32x4 kf = *(const i32x4*)(&Ks[buf][(32 * kt + ql) * KROWB + 32 * s + 16 * hf]);
-          iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], iacc, 0, 0, 0);
+          iacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], iacc[kt], 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lg[kt][r] = __builtin_fmaf((float)iacc[r], sc, bias);
-      }
-    }
-
-    const bool need_mask = (64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N);
-    if (need_mask) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * j + 32 * kt + (r >> 2) * 8 + 4 * hf + (r & 3);
-          if (key >= N || (p.causal && key > t) || !row_ok) lg[kt][r] = kNegInf;
-        }
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = (float)iacc[kt][r];
     }
 
-    float mx = kNegInf;
+    if ((64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N)) {
+      const int rel = lim - 64 * j - 4 * hf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = key_off(kt, r) < rel ? sacc[kt][r] : kNegInf;
+    }
+
+    float mraw = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, lg[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+      for (int r = 0; r < 16; r += 2) mraw = max3f(mraw, sacc[kt][r], sacc[kt][r + 1]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    float mx;  // block max of this row in log2 units, -inf when no key is visible
+    if constexpr (QK8) mx = (mraw == kNegInf) ? kNegInf : __builtin_fmaf(mraw, sc, bias);
+    else mx = mraw * p.c;
+
     if (p.filter_on) {
+      const float m_new = fmaxf(m_true, mx);
       const bool keep = (mx != kNegInf) && (mx - m_new >= p.lam2);
       if (__ballot(keep) == 0ull) {
         ++n_skip;
         continue;
       }
+      m_true = m_new;
     }
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    if (__ballot(mx > m_ref + kTau) != 0ull) {
+      const float m_ref_new = fmaxf(m_ref, mx);
+      const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
+      l_acc *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_ref = m_ref_new;
+      m_use = mu_new;
+    }
 
-    float rs = 0.0f;
-    u16x8 pf[4];
+    // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
+    const float slope = QK8 ? sc : p.c;
+    const float offs = (QK8 ? bias : 0.0f) - m_use;
+    u32x4 pw[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(lg[kt][r] - m_use);
-        rs += pv;
-        pf[2 * kt + (r >> 3)][r & 7] = f32_to_u16<PV_F16>(pv);
-      }
-    l_part = l_part * alpha + rs;
+      for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        for (int wd = 0; wd < 4; ++wd) {
+          const int r = 8 * sg + 2 * wd;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], slope, offs));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r + 1], slope, offs));
+          const unsigned int pr = pack2<PV_F16>(p0, p1);
+          l_acc = add_pair<PV_F16>(pr, l_acc);
+          pw[2 * kt + sg][wd] = pr;
+        }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
-      for (int sg = 0; sg < 4; ++sg) {
+      for (int dt = 0; dt < DT; ++dt) {
         const u16x8 vf = *(const u16x8*)(&Vs[buf][(32 * dt + ql) * VSTR + 16 * sg + 8 * hf]);
-        oacc[dt] = mma16<PV_F16>(vf, pf[sg], oacc[dt]);
+        oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
       }
   }
 
   // epilogue: O = acc / l, this lane's query row, columns 32dt + 8g + 4hf + 0..3
-  const float lt = l_part + __shfl_xor(l_part, 32, 64);
+  const float lt = l_acc + __shfl_xor(l_acc, 32, 64);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     char* ob = (char*)p.o;
@@ -358,11 +418,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         if (p.out_type == kF32) {
           *(float4*)(ob + rowoff + (int64_t)col * 4) = make_float4(o0, o1, o2, o3);
         } else if (p.out_type == kF16) {
-          u16x4 v = {f32_to_u16<true>(o0), f32_to_u16<true>(o1), f32_to_u16<true>(o2), f32_to_u16<true>(o3)};
-          *(u16x4*)(ob + rowoff + (int64_t)col * 2) = v;
+          const uint2 v = {pack2<true>(o0, o1), pack2<true>(o2, o3)};
+          *(uint2*)(ob + rowoff + (int64_t)col * 2) = v;
         } else {
-          u16x4 v = {f32_to_u16<false>(o0), f32_to_u16<false>(o1), f32_to_u16<false>(o2), f32_to_u16<false>(o3)};
-          *(u16x4*)(ob + rowoff + (int64_t)col * 2) = v;
+          const uint2 v = {pack2<false>(o0, o1), pack2<false>(o2, o3)};
+          *(uint2*)(ob + rowoff + (int64_t)col * 2) = v;
         }
       }
   }

@@ -315,9 +315,11 @@ __global__ __launch_bounds__(64) void compact_kernel(const uint8_t* mask, Dims d
   }
 }
 
-// fp32 -> bf16 (round to nearest even) into a contiguous (B, H, N, D) buffer.
-__global__ __launch_bounds__(256) void convert_bf16_kernel(View x, Dims d, uint16_t* dst) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 4-element chunk each
+// Element-type conversion (fp32 / bf16 / fp16 -> bf16 or fp16, round to nearest
+// even) into a contiguous (B, H, N, D) buffer; four elements per thread.
+template <int SRC, bool DST_F16>
+__global__ __launch_bounds__(256) void convert16_kernel(View x, Dims d, uint16_t* dst) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_row = d.D / 4;
   const int64_t total = (int64_t)d.B * d.H * d.N * per_row;
   if (idx >= total) return;
@@ -326,20 +328,26 @@ __global__ __launch_bounds__(256) void convert_bf16_kernel(View x, Dims d, uint1
   const int n = (int)(rowi % d.N);
   const int64_t bhi = rowi / d.N;
   const int b = (int)(bhi / d.H), h = (int)(bhi % d.H);
-  const float4 v = *(const float4*)((const float*)x.p + (int64_t)b * x.sB + (int64_t)h * x.sH +
-                                   (int64_t)n * x.sN + c);
-  const float vals[4] = {v.x, v.y, v.z, v.w};
+  const int64_t src = (int64_t)b * x.sB + (int64_t)h * x.sH + (int64_t)n * x.sN + c;
+  float vals[4];
+  if constexpr (SRC == kF32) {
+    const float4 v = *(const float4*)((const float*)x.p + src);
+    vals[0] = v.x; vals[1] = v.y; vals[2] = v.z; vals[3] = v.w;
+  } else {
+    const ushort4 v = *(const ushort4*)((const unsigned short*)x.p + src);
+    const unsigned short u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vals[e] = (SRC == kF16) ? (float)__builtin_bit_cast(_Float16, u[e])
+                              : __uint_as_float((unsigned int)u[e] << 16);
+  }
+  ushort4 w;
   unsigned short o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const unsigned int u = __float_as_uint(vals[e]);
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-      o[e] = (unsigned short)((u >> 16) | 0x40);  // quiet NaN
-    } else {
-      o[e] = (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    }
+    if constexpr (DST_F16) o[e] = __builtin_bit_cast(unsigned short, (_Float16)vals[e]);
+    else o[e] = __builtin_bit_cast(unsigned short, (__bf16)vals[e]);
   }
-  ushort4 w;
   w.x = o[0]; w.y = o[1]; w.z = o[2]; w.w = o[3];
   *(ushort4*)(dst + rowi * d.D + c) = w;
 }
@@ -395,10 +403,15 @@ hipError_t launch_compact(const uint8_t* mask, const Dims& d, uint16_t* lists, i
   return hipGetLastError();
 }
 
-hipError_t launch_convert_bf16(const View& x, const Dims& d, uint16_t* dst, hipStream_t s) {
+hipError_t launch_convert16(const View& x, int src_dtype, const Dims& d, uint16_t* dst,
+                            int dst_f16, hipStream_t s) {
   const int64_t chunks = (int64_t)d.B * d.H * d.N * (d.D / 4);
   const dim3 grid((unsigned)((chunks + 255) / 256));
-  convert_bf16_kernel<<<grid, 256, 0, s>>>(x, d, dst);
+#define SPARGE_CV(SV, DV) convert16_kernel<SV, DV><<<grid, 256, 0, s>>>(x, d, dst)
+  if (src_dtype == kF32) { if (dst_f16) SPARGE_CV(kF32, true); else SPARGE_CV(kF32, false); }
+  else if (src_dtype == kF16) { if (dst_f16) SPARGE_CV(kF16, true); else SPARGE_CV(kF16, false); }
+  else { if (dst_f16) SPARGE_CV(kBF16, true); else SPARGE_CV(kBF16, false); }
+#undef SPARGE_CV
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ struct Workspace {
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
   size_t lists, counts;            // uint16 kept-block lists (BH, nQ, nK), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
-  size_t conv;                     // bf16 copies of fp32 q, k, v (3 x BH*N*D)
+  size_t conv;                     // 16-bit copies of q, k (fp32 inputs) and v (3 x BH*N*D)
   size_t counters;                 // 8 x uint64 stats counters
   size_t total;
 };
@@ -45,8 +45,10 @@ Workspace plan_workspace(const Dims& d, int dtype);
 // Kernel launchers (return hipSuccess or the launch error).
 // ---------------------------------------------------------------------------
 
-// fp32 -> bf16 (RNE) copy of a strided view into a contiguous (B, H, N, D) buffer.
-hipError_t launch_convert_bf16(const View& x, const Dims& d, uint16_t* dst, hipStream_t s);
+// fp32/bf16/fp16 -> bf16 or fp16 (RNE) copy of a strided view into a contiguous
+// (B, H, N, D) buffer.
+hipError_t launch_convert16(const View& x, int src_dtype, const Dims& d, uint16_t* dst,
+                            int dst_f16, hipStream_t s);
 
 // Per block (Q: 128 rows, K: 64 rows) channel sums in fp64 and self-similarity.
 hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dims& d,
@@ -78,7 +80,8 @@ hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes
                           hipStream_t s);
 
 struct AttnParams {
-  View q, k, v;          // 16-bit (bf16 or fp16) views
+  View q, k;             // 16-bit (bf16 or fp16) views of Q and K
+  View v;                // V in the P.V type (fp16 when pv_fp16, else Q's type)
   void* o;               // output
   int64_t osB, osH, osN;
   int in_f16;            // q/k/v element type: 1 = fp16, 0 = bf16
