@@ -23,7 +23,7 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.ksum = take(BH * d.nK * d.D * sizeof(double));
   w.ksim = take(BH * d.nK * sizeof(double));
   w.scores = take(BH * d.nQ * d.nK * sizeof(double));
-  w.lists = take(BH * d.nQ * d.nK * sizeof(uint16_t));
+  w.lists = take(BH * d.nQ * d.lstride * sizeof(uint16_t));
   w.counts = take(BH * d.nQ * sizeof(int));
   w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
   w.kscale = take(BH * d.nK * sizeof(float));
@@ -62,11 +62,7 @@ bool same_shape(const sparge_tensor* a, const sparge_tensor* b) {
 }
 
 Dims dims_of(const sparge_tensor* t) {
-  Dims d;
-  d.B = (int)t->B; d.H = (int)t->H; d.N = (int)t->N; d.D = (int)t->D;
-  d.nQ = (d.N + 127) / 128;
-  d.nK = (d.N + 63) / 64;
-  return d;
+  return make_dims((int)t->B, (int)t->H, (int)t->N, (int)t->D);
 }
 
 View view_of(const sparge_tensor* t) { return View{t->data, t->sB, t->sH, t->sN}; }
@@ -257,11 +253,7 @@ size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
   (void)opts;
   if (B < 1 || H < 1 || N < 1 || N > kMaxN || (D != 64 && D != 128)) return 0;
   if (dtype != SPARGE_F32 && dtype != SPARGE_F16 && dtype != SPARGE_BF16) return 0;
-  Dims d;
-  d.B = (int)B; d.H = (int)H; d.N = (int)N; d.D = (int)D;
-  d.nQ = (d.N + 127) / 128;
-  d.nK = (d.N + 63) / 64;
-  return plan_workspace(d, dtype).total;
+  return plan_workspace(make_dims((int)B, (int)H, (int)N, (int)D), dtype).total;
 }
 
 sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,

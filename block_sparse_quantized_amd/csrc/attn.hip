@@ -187,7 +187,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   }
 
   const int cnt = p.counts[bh * d.nQ + i];
-  const unsigned short* lst = p.lists + (int64_t)(bh * d.nQ + i) * d.nK;
+  // The row's kept-block list, read through the constant address space so that
+  // the (wave-uniform) reads are scalar loads: they never wait behind the vector
+  // tile prefetches.  Rows are 16-byte aligned; two uint16 entries per dword.
+  typedef const __attribute__((address_space(4))) unsigned int* const_u32_ptr;
+  const const_u32_ptr lst32 = (const_u32_ptr)(p.lists + (int64_t)(bh * d.nQ + i) * d.lstride);
+  auto list_at = [&](int k) -> int {
+    const unsigned int wv = lst32[k >> 1];
+    return (int)((k & 1) ? (wv >> 16) : (wv & 0xffffu));
+  };
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -257,13 +265,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     }
   };
 
-  if (cnt > 0) load_tile(lst[0]);
+  // Block indices travel one and two iterations ahead of their use, so that no
+  // wait on a list read ever drains the tile prefetch queue.
+  int j_cur = cnt > 0 ? list_at(0) : 0;
+  int j_nxt = cnt > 1 ? list_at(1) : 0;
+  if (cnt > 0) load_tile(j_cur);
   for (int it = 0; it < cnt; ++it) {
-    const int j = lst[it];
+    const int j = j_cur;
     const int buf = it & 1;
+    const int j_after = (it + 2 < cnt) ? list_at(it + 2) : 0;
     store_tile(buf);
     __syncthreads();
-    if (it + 1 < cnt) load_tile(lst[it + 1]);
+    if (it + 1 < cnt) load_tile(j_nxt);
+    j_cur = j_nxt;
+    j_nxt = j_after;
 
     float bias = 0.0f;   // int8 path: c * (q . kbar_j) for this lane's query
     float sc = 0.0f;     // int8 path: c * dq * dk_j
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           const int pr = e / (D / 4), c4 = (e % (D / 4)) * 4;
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
           if (it + pr < cnt)
-            v = *(const float4*)(p.kbar + ((int64_t)bh * d.nK + lst[it + pr]) * D + c4);
+            v = *(const float4*)(p.kbar + ((int64_t)bh * d.nK + list_at(it + pr)) * D + c4);
           const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64) void select_kernel(const double* scores, const 
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_before = 0, base = 0;
   uint8_t* mrow = mask_out ? mask_out + row * nK : nullptr;
-  uint16_t* lrow = lists + row * nK;
+  uint16_t* lrow = lists + row * d.lstride;
   for (int j0 = 0; j0 < nK; j0 += 64) {
     const int j = j0 + lane;
     const unsigned f = j < nK ? flags[j] : 0u;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64) void compact_kernel(const uint8_t* mask, Dims d
   const int nK = d.nK;
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int base = 0;
-  uint16_t* lrow = lists + row * nK;
+  uint16_t* lrow = lists + row * d.lstride;
   for (int j0 = 0; j0 < nK; j0 += 64) {
     const int j = j0 + lane;
     const bool keep = j < nK && (mask == nullptr || mask[row * nK + j] != 0);

@@ -23,8 +23,18 @@ struct View {
 
 struct Dims {
   int B, H, N, D;
-  int nQ, nK;  // ceil(N/128), ceil(N/64)
+  int nQ, nK;   // ceil(N/128), ceil(N/64)
+  int lstride;  // elements per kept-block list row: nK rounded up to 8 (16-byte rows)
 };
+
+inline Dims make_dims(int B, int H, int N, int D) {
+  Dims d;
+  d.B = B; d.H = H; d.N = N; d.D = D;
+  d.nQ = (N + kBQ - 1) / kBQ;
+  d.nK = (N + kBK - 1) / kBK;
+  d.lstride = (d.nK + 7) & ~7;
+  return d;
+}
 
 // ---------------------------------------------------------------------------
 // Workspace: one buffer, carved into 256-byte aligned regions.
@@ -32,7 +42,7 @@ struct Dims {
 struct Workspace {
   size_t qsum, qsim, ksum, ksim;   // fp64 block sums and self-similarities
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
-  size_t lists, counts;            // uint16 kept-block lists (BH, nQ, nK), int32 counts
+  size_t lists, counts;            // uint16 kept-block lists (BH, nQ, lstride), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
   size_t conv;                     // 16-bit copies of q, k (fp32 inputs) and v (3 x BH*N*D)
   size_t counters;                 // 8 x uint64 stats counters

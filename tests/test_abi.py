@@ -129,7 +129,7 @@ def test_workspace_bytes(lib):
     a = lib.sparge_workspace_bytes(1, 32, 8192, 128, L.SPARGE_BF16, None)
     b = lib.sparge_workspace_bytes(1, 32, 16384, 128, L.SPARGE_BF16, None)
     c = lib.sparge_workspace_bytes(1, 32, 8192, 128, L.SPARGE_F32, None)
-    assert 0 < a < b and c > a
+    assert 0 < a < b and c >= a
     assert lib.sparge_workspace_bytes(1, 32, 8192, 96, L.SPARGE_BF16, None) == 0
     assert lib.sparge_workspace_bytes(1, 32, 0, 128, L.SPARGE_BF16, None) == 0
     assert lib.sparge_workspace_bytes(1, 32, 8192, 128, 5, None) == 0
