@@ -20,6 +20,8 @@
 //   * grid order: XCD-aware (each of the 8 XCDs gets a contiguous range of
 //     tiles, head-major so co-resident workgroups share K/V in that XCD's L2),
 //     longest causal rows first.
+#include <type_traits>
+
 #include "sparge_internal.hpp"
 
 namespace sparge {
@@ -64,10 +66,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
 }
 
-// Position, inside a 16-key group of the transposed V tile, of the 4-key run that
-// starts at key offset 4*g (g = 0..3): lane half h of the P.V MFMA holds keys
-// {4h..4h+3, 8+4h..8+4h+3} of the group as its 8 consecutive k slots.
-__device__ __forceinline__ int vpos4(int g) { return (g == 1) ? 8 : (g == 2 ? 4 : 4 * g); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -92,32 +90,72 @@ __device__ __forceinline__ float add_pair(unsigned int pr, float acc) {
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Key offset, inside a 64-key block, of register r of key tile kt for lane half 0
-// (half 1 adds 4): the 32x32 MFMA result layout.
-__device__ __forceinline__ constexpr int key_off(int kt, int r) { return 32 * kt + (r >> 2) * 8 + (r & 3); }
 
 // Reference-max slack (log2 units): exponentials are taken against a reference
 // max that moves only when a row's running max exceeds it by more than this, so
 // O and l are rescaled rarely; P then stays below 2^8.
 constexpr float kTau = 8.0f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Key offset, inside a 64-key block, of register r of key tile kt: the K rows fed
+// to the Q.K^T MFMA are permuted (row m of a 32-key tile holds key swap23(m)), so
+// that each lane's eight P values of a P.V k-step are eight consecutive keys.
+// Lane half 1 adds 8.
+__device__ __forceinline__ constexpr int key_off2(int kt, int r) {
+  return 32 * kt + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+}
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Granule swizzles of the LDS tiles (physical granule = logical ^ f(row)), for
+// gfx950's 64-bank LDS (256 bytes per cycle: sixteen lanes of a 16-byte read,
+// thirty-two lanes of an 8-byte read).  K fragment reads: sixteen lanes read one
+// granule column of rows swap23(0..15); fk maps those rows to sixteen different
+// bank groups for 256-, 128- and 64-byte rows.  V transposing reads: thirty-two
+// lanes cover four consecutive rows x four adjacent granules; fv spreads them
+// over sixteen bank groups.
+template <int G>
+__device__ __forceinline__ int fk(int r) {
+  if constexpr (G >= 16) return r & 15;
+  else if constexpr (G == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+template <int G>
+__device__ __forceinline__ int fv(int r) {
+  if constexpr (G >= 16) return 4 * (r & 3);
+  else return 4 * ((r >> 1) & 1);
+}
+
 template <int D, bool IN_F16, bool PV_F16, bool QK8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims d) {
-  constexpr int KS16 = D / 16;                 // k-steps of the 16-bit Q K^T
-  constexpr int KS8 = D / 32;                  // k-steps of the int8 Q K^T
-  constexpr int DT = D / 32;                   // 32-column output tiles
-  constexpr int KROWB = QK8 ? (D + 16) : 2 * (D + 8);  // bytes per staged K row
-  constexpr int VSTR = 64 + 8;                 // u16 elements per transposed V row
-  constexpr int KCPR = QK8 ? D / 16 : D / 8;   // 16-byte chunks per K row
-  constexpr int KCH = 64 * KCPR / 256;         // K chunks per thread
-  constexpr int VTASK = 16 * (D / 8);          // (4-key run, 8-column chunk) tasks
-  constexpr int KBSTR = D + 8;                 // u16 per row of the kbar hi/lo tiles
+  constexpr int KS16 = D / 16;                // k-steps of the 16-bit Q K^T
+  constexpr int KS8 = D / 32;                 // k-steps of the int8 Q K^T
+  constexpr int DT = D / 32;                  // 32-column output tiles
+  constexpr int KROW = QK8 ? D : 2 * D;       // bytes per K row in LDS (no padding)
+  constexpr int VROW = 2 * D;                 // bytes per V row in LDS
+  constexpr int KG = KROW / 16;               // 16-byte granules per K row
+  constexpr int VG = VROW / 16;
+  constexpr int KCHUNK = 64 * KROW / 1024;    // 1 KB DMA chunks per K tile
+  constexpr int VCHUNK = 64 * VROW / 1024;
+  constexpr int KBSTR = D + 8;                // u16 per row of the kbar hi/lo tiles
   constexpr int AUXB = QK8 ? ((2 * 32 * KBSTR * 2) > (4 * 32 * 33 * 4) ? (2 * 32 * KBSTR * 2)
                                                                         : (4 * 32 * 33 * 4))
                            : 16;
-
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[2][64 * KROWB];
-  __shared__ __attribute__((aligned(16))) unsigned short Vs[2][D * VSTR];
+  // LDS tiles are written by direct-to-LDS loads (one 1 KB chunk per wavefront
+  // instruction, lane-linear) and stored row-major with each row's 16-byte granules
+  // XOR-swizzled by a function of the row (fk, fv), so fragment reads are free of
+  // bank conflicts.
+  // One variable per stage and tile: the compiler then knows that a DMA into one
+  // stage never aliases reads of the other, and does not wait for it.
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks0[64 * KROW];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks1[64 * KROW];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs0[64 * VROW];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs1[64 * VROW];
   __shared__ __attribute__((aligned(16))) unsigned char Aux[AUXB];
 
   const int tid = threadIdx.x;
@@ -138,14 +176,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const char* Kb = QK8 ? (const char*)(p.k8 + (int64_t)bh * d.nK * 64 * D)
                        : (const char*)((const unsigned short*)p.k.p + b * p.k.sB + h * p.k.sH);
   const char* Vb = (const char*)((const unsigned short*)p.v.p + b * p.v.sB + h * p.v.sH);
+  const int64_t ksrow = QK8 ? (int64_t)D : p.k.sN * 2;   // bytes between K rows in memory
+  const int64_t vsrow = p.v.sN * 2;
 
   // Q fragments in the B-operand layout: lane (hf, ql) holds Q[t][16s + 8hf .. +7].
-  u16x8 qf[KS16];
+  // The int8 path needs them only for the q . kbar term every 32 blocks and
+  // reloads them there, to keep registers for the pipeline.
+  auto load_qf = [&](u16x8 (&f)[KS16]) {
 #pragma unroll
-  for (int s = 0; s < KS16; ++s) {
-    if (row_ok) qf[s] = *(const u16x8*)(Qp + (int64_t)t * p.q.sN + 16 * s + 8 * hf);
-    else qf[s] = (u16x8)(0);
-  }
+    for (int s = 0; s < KS16; ++s) {
+      if (row_ok) f[s] = *(const u16x8*)(Qp + (int64_t)t * p.q.sN + 16 * s + 8 * hf);
+      else f[s] = (u16x8)(0);
+    }
+  };
+  u16x8 qf[QK8 ? 1 : KS16];
+  if constexpr (!QK8) load_qf(qf);
 
   // int8 Q codes: lane holds Q[t][32s + 16hf .. +15], one step per wavefront.
   i32x4 q8[QK8 ? KS8 : 1];
@@ -188,8 +233,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 
   const int cnt = p.counts[bh * d.nQ + i];
   // The row's kept-block list, read through the constant address space so that
-  // the (wave-uniform) reads are scalar loads: they never wait behind the vector
-  // tile prefetches.  Rows are 16-byte aligned; two uint16 entries per dword.
+  // the (wave-uniform) reads are scalar loads that never wait behind vector loads.
   typedef const __attribute__((address_space(4))) unsigned int* const_u32_ptr;
   const const_u32_ptr lst32 = (const_u32_ptr)(p.lists + (int64_t)(bh * d.nQ + i) * d.lstride);
   auto list_at = [&](int k) -> int {
@@ -206,82 +250,129 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   float l_acc = 0.0f;       // this lane's partial row sum (its half of the keys)
   unsigned int n_skip = 0;
 
-  // per-thread staging addresses (bytes from the head base), fixed over the loop
-  int koff[KCH], krow[KCH];
+  // Direct-to-LDS loads of one block's K tile (into K stage KS) or V tile (into V
+  // stage VS): wavefront w issues chunks w, w+4, ... of the tile; lane l of chunk c
+  // fills LDS bytes 1024c + 16l, i.e. row r = c*1024/ROW + l/G, physical granule
+  // l%G, holding logical granule (l%G) ^ f(r).  Rows past N (ragged last block)
+  // re-read row N-1; their scores are masked, so they contribute exactly zero.
+  auto dma_k = [&](int j, auto kstage) {
+    unsigned char* dst = decltype(kstage)::value ? Ks1 : Ks0;
+    const int row0 = 64 * j;
 #pragma unroll
-  for (int u = 0; u < KCH; ++u) {
-    const int c = tid + 256 * u;
-    krow[u] = c / KCPR;
-    koff[u] = QK8 ? krow[u] * D + 16 * (c % KCPR) : (krow[u] * (int)p.k.sN + 8 * (c % KCPR)) * 2;
-  }
-  // V staging task of this thread: 4-key run g4 (16 per block) x 8-column chunk dc.
-  // Sixteen consecutive lanes take the sixteen runs of one chunk, so each
-  // transposed LDS store instruction covers whole 128-byte rows (no bank conflicts).
-  const bool vtask = (VTASK == 256) || (tid < VTASK);
-  const int g4 = tid & 15, dc = tid >> 4;
-  const int voff = (4 * g4 * (int)p.v.sN + 8 * dc) * 2;
-  const int vrow = (int)p.v.sN * 2;
-  const int64_t kblk = QK8 ? (int64_t)64 * D : (int64_t)64 * p.k.sN * 2;
-  const int64_t vblk = (int64_t)64 * p.v.sN * 2;
-
-  u16x8 kreg[KCH];
-  u16x8 vreg[4];
-
-  auto load_tile = [&](int j) {
-    const char* kb = Kb + j * kblk;
-    const char* vb = Vb + j * vblk;
-    if (QK8 || 64 * j + 64 <= N) {
+    for (int c = w; c < KCHUNK; c += 4) {
+      const int r = c * (1024 / KROW) + lane / KG;
+      const int pg = lane % KG;
+      const int lg = pg ^ fk<KG>(r);
+      const int rr = QK8 ? row0 + r : min(row0 + r, N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(Kb + rr * ksrow + 16 * lg),
+                                       (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
+    }
+  };
+  auto dma_v = [&](int j, auto vstage) {
+    unsigned char* dst = decltype(vstage)::value ? Vs1 : Vs0;
+    const int row0 = 64 * j;
 #pragma unroll
-      for (int u = 0; u < KCH; ++u) kreg[u] = *(const u16x8*)(kb + koff[u]);
-      if (vtask) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[r] = *(const u16x8*)(vb + voff + r * vrow);
-      }
-    } else {  // ragged last block: rows past N read as zeros
-#pragma unroll
-      for (int u = 0; u < KCH; ++u)
-        kreg[u] = (64 * j + krow[u] < N) ? *(const u16x8*)(kb + koff[u]) : (u16x8)(0);
-      if (vtask) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[r] = (64 * j + 4 * g4 + r < N) ? *(const u16x8*)(vb + voff + r * vrow) : (u16x8)(0);
-      }
+    for (int c = w; c < VCHUNK; c += 4) {
+      const int r = c * (1024 / VROW) + lane / VG;
+      const int pg = lane % VG;
+      const int lg = pg ^ fv<VG>(r);
+      const int rr = min(row0 + r, N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(Vb + rr * vsrow + 16 * lg),
+                                       (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
     }
   };
 
-  auto store_tile = [&](int buf) {
+  // per-lane row of the Q.K^T A fragments: 32kt + swap23(ql), granule 2s+hf
+  const int krow_l = swap23(ql);
+  typedef std::conditional_t<QK8, i32x16, f32x16> acc_t;
+
+  // Raw Q.K^T of the block staged in K stage KS (MFMAs only; no waits on results).
+  auto qk = [&](auto kstage, acc_t (&acc)[2]) {
+    const unsigned char* Kst = decltype(kstage)::value ? Ks1 : Ks0;
+    acc[0] = (acc_t)(0);
+    acc[1] = (acc_t)(0);
+    if constexpr (!QK8) {
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + 256 * u;
-      *(u16x8*)(&Ks[buf][(c / KCPR) * KROWB + 16 * (c % KCPR)]) = kreg[u];
-    }
-    if (vtask) {
-      const int pos = 16 * (g4 >> 2) + vpos4(g4 & 3);
+      for (int s = 0; s < KS16; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const u16x4 v4 = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *(u16x4*)(&Vs[buf][(8 * dc + e) * VSTR + pos]) = v4;
-      }
+        for (int kt = 0; kt < 2; ++kt) {
+          const int rr = 32 * kt + krow_l;
+          const int pg = (2 * s + hf) ^ fk<KG>(rr);
+          const u16x8 kf = *(const u16x8*)(Kst + rr * KROW + 16 * pg);
+          acc[kt] = mma16<IN_F16>(kf, qf[s], acc[kt]);
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS8; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int rr = 32 * kt + krow_l;
+          const int pg = (2 * s + hf) ^ fk<KG>(rr);
+          const i32x4 kf = *(const i32x4*)(Kst + rr * KROW + 16 * pg);
+          acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], acc[kt], 0, 0, 0);
+        }
     }
   };
 
-  // Block indices travel one and two iterations ahead of their use, so that no
-  // wait on a list read ever drains the tile prefetch queue.
-  int j_cur = cnt > 0 ? list_at(0) : 0;
-  int j_nxt = cnt > 1 ? list_at(1) : 0;
-  if (cnt > 0) load_tile(j_cur);
-  for (int it = 0; it < cnt; ++it) {
-    const int j = j_cur;
-    const int buf = it & 1;
-    const int j_after = (it + 2 < cnt) ? list_at(it + 2) : 0;
-    store_tile(buf);
+  // Scores as fp32 with invisible keys at -inf, and the row max of the raw scores
+  // (both lane halves); key of sc[kt][r] is 64j + 8hf + key_off2(kt, r).
+  auto mask_max = [&](const acc_t (&acc)[2], int j, f32x16 (&sc)[2]) -> float {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kt][r] = (float)acc[kt][r];
+    if ((64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N)) {
+      const int rel = lim - 64 * j - 8 * hf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][r] = key_off2(kt, r) < rel ? sc[kt][r] : kNegInf;
+    }
+    float mraw = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mraw = max3f(mraw, sc[kt][r], sc[kt][r + 1]);
+    return fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+  };
+
+  // Software pipeline over the kept blocks.  Step `it` (block j = list[it]):
+  //   wait for K(it+1) and V(it) -> barrier -> DMA K(it+2) and V(it+1) ->
+  //   issue Q.K^T of block it+1 -> softmax of block it (its mask/max were done
+  //   during the previous step) -> P.V of block it -> mask/max of block it+1.
+  // K is staged two blocks ahead and V one block ahead in two stages each; every
+  // stage is its own LDS variable and the loop is unrolled by two, so no DMA ever
+  // targets a stage that is being read in the same step.
+  std::integral_constant<int, 0> s0;
+  std::integral_constant<int, 1> s1;
+  int j_cur = cnt > 0 ? list_at(0) : 0;   // block of step it
+  int j_n1 = cnt > 1 ? list_at(1) : 0;    // block it+1
+  int j_n2 = cnt > 2 ? list_at(2) : 0;    // block it+2
+  acc_t acc_cur[2];
+  f32x16 sc_cur[2];
+  float mraw_cur = kNegInf;
+  if (cnt > 0) {
+    dma_k(j_cur, s0);
+    if (cnt > 1) dma_k(j_n1, s1);
+    dma_v(j_cur, s0);
+    wait_vmem_all();
     __syncthreads();
-    if (it + 1 < cnt) load_tile(j_nxt);
-    j_cur = j_nxt;
-    j_nxt = j_after;
+    qk(s0, acc_cur);
+    mraw_cur = mask_max(acc_cur, j_cur, sc_cur);
+  }
 
+  auto step = [&](int it, auto par) {
+    constexpr int P = decltype(par)::value;        // it & 1
+    std::integral_constant<int, P> sp;
+    std::integral_constant<int, 1 - P> sq;
+    const int j = j_cur;
+    const int j_n3 = (it + 3 < cnt) ? list_at(it + 3) : 0;
+    wait_vmem_all();     // this wavefront's DMAs of K(it+1) and V(it) have landed
+    __syncthreads();     // ... and every wavefront's; K stage P and V stage 1-P are free
+    if (it + 2 < cnt) dma_k(j_n2, sp);
+    if (it + 1 < cnt) dma_v(j_n1, sq);
     float bias = 0.0f;   // int8 path: c * (q . kbar_j) for this lane's query
-    float sc = 0.0f;     // int8 path: c * dq * dk_j
+    float slope_i8 = 0.0f;
     if constexpr (QK8) {
       unsigned short* kbh = (unsigned short*)Aux;            // [32][KBSTR] hi
       unsigned short* kbl = kbh + 32 * KBSTR;                // [32][KBSTR] lo
@@ -304,13 +395,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           }
         }
         __syncthreads();
+        u16x8 qfr[KS16];
+        load_qf(qfr);
         f32x16 cacc = (f32x16)(0.0f);
 #pragma unroll
         for (int s = 0; s < KS16; ++s) {
           const u16x8 ah = *(const u16x8*)(kbh + ql * KBSTR + 16 * s + 8 * hf);
           const u16x8 al = *(const u16x8*)(kbl + ql * KBSTR + 16 * s + 8 * hf);
-          cacc = mma16<IN_F16>(ah, qf[s], cacc);
-          cacc = mma16<IN_F16>(al, qf[s], cacc);
+          cacc = mma16<IN_F16>(ah, qfr[s], cacc);
+          cacc = mma16<IN_F16>(al, qfr[s], cacc);
         }
         __syncthreads();  // every wave is done reading kbh/kbl, which cw overlays
         // lane (hf, ql) holds C[block (r/4)*8 + 4hf + r%4][query ql]
@@ -321,99 +414,87 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       bias = p.c * cw[(it & 31) * 33 + ql];
       // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
       // that masked (-inf) scores stay -inf
-      sc = fmaxf(p.c * dq * p.kscale[(int64_t)bh * d.nK + j], 1e-30f);
+      slope_i8 = fmaxf(p.c * dq * p.kscale[(int64_t)bh * d.nK + j], 1e-30f);
     }
+    acc_t acc_nxt[2];
+    if (it + 1 < cnt) qk(sq, acc_nxt);
 
-    // raw scores of this lane's query against the block's 64 keys:
-    // sacc[kt][r] is key 64j + 4hf + key_off(kt, r)
-    f32x16 sacc[2];
-    if constexpr (!QK8) {
-      sacc[0] = (f32x16)(0.0f);
-      sacc[1] = (f32x16)(0.0f);
-#pragma unroll
-      for (int s = 0; s < KS16; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const u16x8 kf = *(const u16x8*)(&Ks[buf][(32 * kt + ql) * KROWB + 32 * s + 16 * hf]);
-          sacc[kt] = mma16<IN_F16>(kf, qf[s], sacc[kt]);
-        }
-    } else {
-      i32x16 iacc[2] = {(i32x16)(0), (i32x16)(0)};
-#pragma unroll
-      for (int s = 0; s < KS8; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const i32x4 kf = *(const i32x4*)(&Ks[buf][(32 * kt + ql) * KROWB + 32 * s + 16 * hf]);
-          iacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], iacc[kt], 0, 0, 0);
-        }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][r] = (float)iacc[kt][r];
-    }
+    // block max of this row in log2 units, -inf when no key is visible
+    float mx;
+    if constexpr (QK8) mx = (mraw_cur == kNegInf) ? kNegInf : __builtin_fmaf(mraw_cur, slope_i8, bias);
+    else mx = mraw_cur * p.c;
 
-    if ((64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N)) {
-      const int rel = lim - 64 * j - 4 * hf;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][r] = key_off(kt, r) < rel ? sacc[kt][r] : kNegInf;
-    }
-
-    float mraw = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mraw = max3f(mraw, sacc[kt][r], sacc[kt][r + 1]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
-    float mx;  // block max of this row in log2 units, -inf when no key is visible
-    if constexpr (QK8) mx = (mraw == kNegInf) ? kNegInf : __builtin_fmaf(mraw, sc, bias);
-    else mx = mraw * p.c;
-
+    bool skip = false;
     if (p.filter_on) {
       const float m_new = fmaxf(m_true, mx);
       const bool keep = (mx != kNegInf) && (mx - m_new >= p.lam2);
       if (__ballot(keep) == 0ull) {
         ++n_skip;
-        continue;
+        skip = true;
+      } else {
+        m_true = m_new;
       }
-      m_true = m_new;
     }
-    if (__ballot(mx > m_ref + kTau) != 0ull) {
-      const float m_ref_new = fmaxf(m_ref, mx);
-      const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
-      l_acc *= alpha;
+    if (!skip) {
+      if (__ballot(mx > m_ref + kTau) != 0ull) {
+        const float m_ref_new = fmaxf(m_ref, mx);
+        const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
+        l_acc *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      m_ref = m_ref_new;
-      m_use = mu_new;
-    }
-
-    // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
-    const float slope = QK8 ? sc : p.c;
-    const float offs = (QK8 ? bias : 0.0f) - m_use;
-    u32x4 pw[4];
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_ref = m_ref_new;
+        m_use = mu_new;
+      }
+      // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
+      const float slope = QK8 ? slope_i8 : p.c;
+      const float offs = (QK8 ? bias : 0.0f) - m_use;
+      u32x4 pw[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
+        for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const int r = 8 * sg + 2 * wd;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], slope, offs));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r + 1], slope, offs));
-          const unsigned int pr = pack2<PV_F16>(p0, p1);
-          l_acc = add_pair<PV_F16>(pr, l_acc);
-          pw[2 * kt + sg][wd] = pr;
+          for (int wd = 0; wd < 4; ++wd) {
+            const int r = 8 * sg + 2 * wd;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
+            const unsigned int pr = pack2<PV_F16>(p0, p1);
+            l_acc = add_pair<PV_F16>(pr, l_acc);
+            pw[2 * kt + sg][wd] = pr;
+          }
+      // V^T fragments by transposing LDS reads: for k-step sg (keys 16sg..16sg+15),
+      // tile dt, lane group g = lane/16 and k = lane%16, read q in {0, 1} covers keys
+      // 16sg + 8(g/2) + 4q + k/4, columns 32dt + 16(g&1) + 4(k&3) .. +3.
+      const unsigned char* Vst = P ? Vs1 : Vs0;
+      const int gq = lane >> 4, kq = lane & 15;
+#pragma unroll
+      for (int sg = 0; sg < 4; ++sg)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          s16x4 part[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int vr = 16 * sg + 8 * (gq >> 1) + 4 * q + (kq >> 2);
+            const int col = 32 * dt + 16 * (gq & 1) + 4 * (kq & 3);
+            const int pg = (col >> 3) ^ fv<VG>(vr);
+            part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Vst + vr * VROW + 16 * pg + 2 * (col & 7)));
+          }
+          const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
         }
-#pragma unroll
-    for (int sg = 0; sg < 4; ++sg)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u16x8 vf = *(const u16x8*)(&Vs[buf][(32 * dt + ql) * VSTR + 16 * sg + 8 * hf]);
-        oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
-      }
+    }
+    // the next block's scores: mask and max while the P.V MFMAs run
+    if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_cur);
+    j_cur = j_n1;
+    j_n1 = j_n2;
+    j_n2 = j_n3;
+  };
+
+  for (int it = 0; it < cnt; it += 2) {
+    step(it, s0);
+    if (it + 1 < cnt) step(it + 1, s1);
   }
 
   // epilogue: O = acc / l, this lane's query row, columns 32dt + 8g + 4hf + 0..3
