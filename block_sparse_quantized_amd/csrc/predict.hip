@@ -209,9 +209,10 @@ __device__ __forceinline__ int keep_count(int C, double topk) {
 }
 
 // One wavefront per block row (b, h, i).  Candidate keys sit in LDS; the k-th
-// largest key is found exactly by a 64-step bitwise search, ties at the threshold
-// go to the lowest block indices, and the kept blocks are compacted in ascending
-// order with ballots.
+// largest key is found exactly by an 8-pass radix select (8-bit digits from the
+// most significant, an LDS histogram per pass and a wavefront suffix scan), ties at
+// the threshold go to the lowest block indices, and the kept blocks are compacted
+// in ascending order with ballots.
 __global__ __launch_bounds__(64) void select_kernel(const double* scores, const double* qsim,
                                                     const double* ksim, Dims d, int causal,
                                                     double topk, double theta, uint8_t* mask_out,
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(64) void select_kernel(const double* scores, const 
                                                     unsigned long long* counters) {
   extern __shared__ unsigned long long keys[];  // nK entries
   unsigned char* flags = (unsigned char*)(keys + d.nK);  // bit0 valid, bit1 similar-K
+  __shared__ unsigned int hist[256];
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
@@ -235,30 +237,58 @@ __global__ __launch_bounds__(64) void select_kernel(const double* scores, const 
     keys[j] = (valid && simk) ? order_key(srow[j]) : 0ull;
     cand_local += (valid && simk) ? 1 : 0;
   }
-  __syncthreads();
-  int C = 0;
   for (int off = 32; off >= 1; off >>= 1) cand_local += __shfl_xor(cand_local, off, 64);
-  C = cand_local;
+  const int C = cand_local;
   const int kk = keep_count(C, topk);
-  unsigned long long T = 0ull;
+  const int jhi = (jv < nK) ? jv : nK;  // candidates only exist below jv
+  unsigned long long T = 0ull, pmask = 0ull;
   int need = 0;
   if (kk > 0) {
-    for (int bit = 63; bit >= 0; --bit) {
-      const unsigned long long trial = T | (1ull << bit);
-      int cnt = 0;
-      for (int j0 = 0; j0 < nK; j0 += 64) {
-        const int j = j0 + lane;
-        const bool ok = j < nK && flags[j] == 3 && keys[j] >= trial;
-        cnt += __popcll(__ballot(ok));
+    int krem = kk;  // rank still to be located among keys matching the prefix
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+      __syncthreads();
+      for (int j = lane; j < jhi; j += 64) {
+        if (flags[j] == 3) {
+          const unsigned long long key = keys[j];
+          if ((key & pmask) == T) atomicAdd(&hist[(unsigned int)(key >> shift) & 255u], 1u);
+        }
       }
-      if (cnt >= kk) T = trial;
+      __syncthreads();
+      // lane l owns digits 255-4l .. 252-4l (descending); suffix counts by scan
+      unsigned int c[4], tot = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hist[255 - (4 * lane + e)];
+        tot += c[e];
+      }
+      unsigned int incl = tot;
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      unsigned int run = incl - tot;  // keys with a larger digit than this lane's range
+      int found = -1;
+      unsigned int above = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (found < 0 && run + c[e] >= (unsigned int)krem) {
+          found = 255 - (4 * lane + e);
+          above = run;
+        }
+        run += c[e];
+      }
+      const unsigned long long fm = __ballot(found >= 0);
+      const int src = __ffsll((long long)fm) - 1;
+      const int dsel = __shfl(found, src, 64);
+      const unsigned int abv = __shfl(above, src, 64);
+      T |= (unsigned long long)dsel << shift;
+      pmask |= 255ull << shift;
+      krem -= (int)abv;
+      __syncthreads();
     }
-    int gt = 0;
-    for (int j0 = 0; j0 < nK; j0 += 64) {
-      const int j = j0 + lane;
-      gt += __popcll(__ballot(j < nK && flags[j] == 3 && keys[j] > T));
-    }
-    need = kk - gt;
+    need = krem;  // keys equal to T still to take (lowest block index first)
   }
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_before = 0, base = 0;

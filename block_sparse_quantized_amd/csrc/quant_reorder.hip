@@ -36,7 +36,9 @@ __device__ __forceinline__ signed char quant_code(float x, float inv) {
   return (signed char)(int)c;
 }
 
-// One wavefront per (b, h, K block).  Lane owns D/64 channels.
+// One wavefront per (b, h, K block), one pass over K: lane owns D/64 channels and
+// keeps the block's 64 rows of them in registers (sums in fp64 in row order, then
+// the mean, the max deviation and the codes, all from registers).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void quant_k_kernel(View k, Dims d, int8_t* codes,
                                                       int64_t crow, int64_t chead, int64_t rows_alloc,
@@ -49,38 +51,45 @@ __global__ __launch_bounds__(256) void quant_k_kernel(View k, Dims d, int8_t* co
   const int b = bh / d.H, h = bh % d.H;
   const int r0 = j * kBK, n = min(kBK, d.N - r0);
   const int64_t base = (int64_t)b * k.sB + (int64_t)h * k.sH + (int64_t)r0 * k.sN;
+  float x[kBK][CPL];
+#pragma unroll
+  for (int r = 0; r < kBK; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      x[r][c] = (r < n) ? ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c) : 0.0f;
   double s[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) s[c] = 0.0;
-  for (int r = 0; r < n; ++r) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = s[c] + (double)ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c);
-  }
+  for (int r = 0; r < kBK; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      if (r < n) s[c] = s[c] + (double)x[r][c];
   float mean[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) mean[c] = (float)(s[c] / (double)n);
   float a = 0.0f;
-  for (int r = 0; r < n; ++r) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float x = ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c) - mean[c];
-      a = fmaxf(a, fabsf(x));
-    }
-  }
+  for (int r = 0; r < kBK; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      if (r < n) a = fmaxf(a, fabsf(x[r][c] - mean[c]));
   a = wave_max_f32(a);
   const float inv = a > 0.0f ? 127.0f / a : 0.0f;
   int8_t* cb = codes + (int64_t)bh * chead;
+#pragma unroll
   for (int r = 0; r < kBK; ++r) {
     const int64_t row = (int64_t)r0 + r;
     if (row >= rows_alloc) break;
+    signed char cc[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      signed char code = 0;
-      if (r < n && a > 0.0f) {
-        const float x = ldf<DT>(k.p, base + (int64_t)r * k.sN + CPL * lane + c) - mean[c];
-        code = quant_code(x, inv);
-      }
-      cb[row * crow + CPL * lane + c] = code;
+    for (int c = 0; c < CPL; ++c)
+      cc[c] = (r < n && a > 0.0f) ? quant_code(x[r][c] - mean[c], inv) : (signed char)0;
+    if constexpr (CPL == 2) {
+      const unsigned short packed = (unsigned short)((unsigned char)cc[0] | ((unsigned char)cc[1] << 8));
+      *(unsigned short*)(cb + row * crow + 2 * lane) = packed;
+    } else {
+      cb[row * crow + lane] = cc[0];
     }
   }
   if (lane == 0) kscale[(int64_t)bh * d.nK + j] = a > 0.0f ? a / 127.0f : 0.0f;
