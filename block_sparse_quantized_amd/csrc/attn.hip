@@ -90,6 +90,17 @@ __device__ __forceinline__ float add_pair(unsigned int pr, float acc) {
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// Lane l ^ 32's value (v_permlane32_swap: the two lane halves trade places).
+__device__ __forceinline__ float partner32(float v, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(hf ? r[0] : r[1]);
+}
+// max(v, value of lane l ^ 32): one of the two swapped copies is v itself.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max3f(v, __uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 
 // Reference-max slack (log2 units): exponentials are taken against a reference
 // max that moves only when a row's running max exceeds it by more than this, so
@@ -98,7 +109,33 @@ constexpr float kTau = 8.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+typedef __attribute__((address_space(3))) unsigned char* lds_u8_ptr;
+
+// Transposing 64-bit LDS read (ds_read_b64_tr_b16) at a per-lane LDS address plus
+// an immediate offset.  Issued as inline asm so that the compiler's wait-count pass,
+// which cannot tell the builtin's LDS reads apart from the direct-to-LDS loads in
+// flight, does not insert a full vector-memory wait in front of it; the caller
+// waits for the result itself with lds_wait.
+template <int OFF>
+__device__ __forceinline__ s16x4 ds_read_tr(unsigned int addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Wait until at most N LDS reads issued after the ones producing a and b are in
+// flight (LDS returns in order, so this makes a and b valid); the asm operands tie
+// the wait to its consumers.
+template <int N>
+__device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -142,6 +179,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   constexpr int VG = VROW / 16;
   constexpr int KCHUNK = 64 * KROW / 1024;    // 1 KB DMA chunks per K tile
   constexpr int VCHUNK = 64 * VROW / 1024;
+  constexpr int kNU = 4 * DT;                 // (k-step, column tile) pairs of P.V
+  constexpr int kVAhead = 4;                  // P.V pairs whose V reads run ahead
   constexpr int KBSTR = D + 8;                // u16 per row of the kbar hi/lo tiles
   constexpr int AUXB = QK8 ? ((2 * 32 * KBSTR * 2) > (4 * 32 * 33 * 4) ? (2 * 32 * KBSTR * 2)
                                                                         : (4 * 32 * 33 * 4))
@@ -159,7 +198,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   __shared__ __attribute__((aligned(16))) unsigned char Aux[AUXB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, hf = lane >> 5, ql = lane & 31;
+  const int lane = tid & 63, hf = lane >> 5, ql = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int bh = tile / d.nQ;
   const int ii = tile - bh * d.nQ;
@@ -240,6 +280,27 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     const unsigned int wv = lst32[k >> 1];
     return (int)((k & 1) ? (wv >> 16) : (wv & 0xffffu));
   };
+  // int8 K steps of this head's blocks, read the same way (scalar loads)
+  typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+  const const_f32_ptr ksc = (const_f32_ptr)(p.kscale + (QK8 ? (int64_t)bh * d.nK : 0));
+  auto kscale_at = [&](int j) -> float { return ksc[j]; };
+
+  // LDS addresses of this lane's transposing V reads per 32-column tile dt (row
+  // 8(g/2) + k/4 of a k-step, granule swizzled as the DMA stores it), per stage;
+  // k-step sg and read q add the immediate offset (16sg + 4q) rows.
+  const int gq = lane >> 4, kq = lane & 15;
+  unsigned int va0[DT], va1[DT];
+  {
+    const int vr = 8 * (gq >> 1) + (kq >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int col = 32 * dt + 16 * (gq & 1) + 4 * (kq & 3);
+      const int pg = (col >> 3) ^ fv<VG>(vr);
+      const int off = vr * VROW + 16 * pg + 2 * (col & 7);
+      va0[dt] = (unsigned int)(size_t)(lds_u8_ptr)Vs0 + off;
+      va1[dt] = (unsigned int)(size_t)(lds_u8_ptr)Vs1 + off;
+    }
+  }
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -255,30 +316,49 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // fills LDS bytes 1024c + 16l, i.e. row r = c*1024/ROW + l/G, physical granule
   // l%G, holding logical granule (l%G) ^ f(r).  Rows past N (ragged last block)
   // re-read row N-1; their scores are masked, so they contribute exactly zero.
+  // Per-lane byte offsets of this wavefront's chunks (c = 4cc + w) inside a full
+  // block; the block's base address is wave-uniform, so each load is a scalar base
+  // plus one 32-bit vector offset.
+  constexpr int KCW = KCHUNK / 4, VCW = VCHUNK / 4;
+  unsigned int koff[KCW], voff[VCW];
+#pragma unroll
+  for (int cc = 0; cc < KCW; ++cc) {
+    const int r = (4 * cc + w) * (1024 / KROW) + lane / KG;
+    koff[cc] = (unsigned int)(r * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+  }
+#pragma unroll
+  for (int cc = 0; cc < VCW; ++cc) {
+    const int r = (4 * cc + w) * (1024 / VROW) + lane / VG;
+    voff[cc] = (unsigned int)(r * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+  }
   auto dma_k = [&](int j, auto kstage) {
     unsigned char* dst = decltype(kstage)::value ? Ks1 : Ks0;
-    const int row0 = 64 * j;
+    const char* base = Kb + (int64_t)(64 * j) * ksrow;
+    const bool full = QK8 || (64 * j + 64 <= N);
 #pragma unroll
-    for (int c = w; c < KCHUNK; c += 4) {
-      const int r = c * (1024 / KROW) + lane / KG;
-      const int pg = lane % KG;
-      const int lg = pg ^ fk<KG>(r);
-      const int rr = QK8 ? row0 + r : min(row0 + r, N - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(Kb + rr * ksrow + 16 * lg),
-                                       (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
+    for (int cc = 0; cc < KCW; ++cc) {
+      const int c = 4 * cc + w;
+      unsigned int off = koff[cc];
+      if (!full) {
+        const int r = c * (1024 / KROW) + lane / KG;
+        off = (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
     }
   };
   auto dma_v = [&](int j, auto vstage) {
     unsigned char* dst = decltype(vstage)::value ? Vs1 : Vs0;
-    const int row0 = 64 * j;
+    const char* base = Vb + (int64_t)(64 * j) * vsrow;
+    const bool full = 64 * j + 64 <= N;
 #pragma unroll
-    for (int c = w; c < VCHUNK; c += 4) {
-      const int r = c * (1024 / VROW) + lane / VG;
-      const int pg = lane % VG;
-      const int lg = pg ^ fv<VG>(r);
-      const int rr = min(row0 + r, N - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(Vb + rr * vsrow + 16 * lg),
-                                       (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
+    for (int cc = 0; cc < VCW; ++cc) {
+      const int c = 4 * cc + w;
+      unsigned int off = voff[cc];
+      if (!full) {
+        const int r = c * (1024 / VROW) + lane / VG;
+        off = (unsigned int)(min(r, N - 1 - 64 * j) * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
     }
   };
 
@@ -333,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mraw = max3f(mraw, sc[kt][r], sc[kt][r + 1]);
-    return fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    return max_xor32(mraw);
   };
 
   // Software pipeline over the kept blocks.  Step `it` (block j = list[it]):
@@ -351,6 +431,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   acc_t acc_cur[2];
   f32x16 sc_cur[2];
   float mraw_cur = kNegInf;
+  float ks_cur = (QK8 && cnt > 0) ? kscale_at(j_cur) : 0.0f;
   if (cnt > 0) {
     dma_k(j_cur, s0);
     if (cnt > 1) dma_k(j_n1, s1);
@@ -367,6 +448,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     std::integral_constant<int, 1 - P> sq;
     const int j = j_cur;
     const int j_n3 = (it + 3 < cnt) ? list_at(it + 3) : 0;
+    const float ks_nxt = QK8 ? kscale_at(j_n1) : 0.0f;   // K step of the next block
     wait_vmem_all();     // this wavefront's DMAs of K(it+1) and V(it) have landed
     __syncthreads();     // ... and every wavefront's; K stage P and V stage 1-P are free
     if (it + 2 < cnt) dma_k(j_n2, sp);
@@ -414,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       bias = p.c * cw[(it & 31) * 33 + ql];
       // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
       // that masked (-inf) scores stay -inf
-      slope_i8 = fmaxf(p.c * dq * p.kscale[(int64_t)bh * d.nK + j], 1e-30f);
+      slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f);
     }
     acc_t acc_nxt[2];
     if (it + 1 < cnt) qk(sq, acc_nxt);
@@ -446,6 +528,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         m_ref = m_ref_new;
         m_use = mu_new;
       }
+      // V^T fragments by transposing LDS reads: for k-step sg (keys 16sg..16sg+15),
+      // tile dt, lane group g = lane/16 and k = lane%16, read q in {0, 1} covers keys
+      // 16sg + 8(g/2) + 4q + k/4, columns 32dt + 16(g&1) + 4(k&3) .. +3.  The (sg, dt)
+      // pairs u = DT*sg + dt run in order with kVAhead pairs' reads in flight; the
+      // first ones are issued before the exponentials.
+      const unsigned int* va = P ? va1 : va0;
+      s16x4 fr[kVAhead + 1][2];
+      auto issue = [&](auto uc) {
+        constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
+        fr[u % (kVAhead + 1)][0] = ds_read_tr<16 * sg * VROW>(va[dt]);
+        fr[u % (kVAhead + 1)][1] = ds_read_tr<(16 * sg + 4) * VROW>(va[dt]);
+      };
+      static_for<0, kVAhead>(issue);
+      __builtin_amdgcn_sched_barrier(0);   // keep these reads ahead of the exponentials
       // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
       const float slope = QK8 ? slope_i8 : p.c;
       const float offs = (QK8 ? bias : 0.0f) - m_use;
@@ -463,33 +559,23 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
             l_acc = add_pair<PV_F16>(pr, l_acc);
             pw[2 * kt + sg][wd] = pr;
           }
-      // V^T fragments by transposing LDS reads: for k-step sg (keys 16sg..16sg+15),
-      // tile dt, lane group g = lane/16 and k = lane%16, read q in {0, 1} covers keys
-      // 16sg + 8(g/2) + 4q + k/4, columns 32dt + 16(g&1) + 4(k&3) .. +3.
-      const unsigned char* Vst = P ? Vs1 : Vs0;
-      const int gq = lane >> 4, kq = lane & 15;
-#pragma unroll
-      for (int sg = 0; sg < 4; ++sg)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          s16x4 part[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int vr = 16 * sg + 8 * (gq >> 1) + 4 * q + (kq >> 2);
-            const int col = 32 * dt + 16 * (gq & 1) + 4 * (kq & 3);
-            const int pg = (col >> 3) ^ fv<VG>(vr);
-            part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_ptr)(Vst + vr * VROW + 16 * pg + 2 * (col & 7)));
-          }
-          const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
-        }
+      static_for<0, kNU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
+        if constexpr (u + kVAhead < kNU) issue(std::integral_constant<int, u + kVAhead>{});
+        constexpr int later = (kNU - 1 - u) < kVAhead ? (kNU - 1 - u) : kVAhead;
+        s16x4& f0 = fr[u % (kVAhead + 1)][0];
+        s16x4& f1 = fr[u % (kVAhead + 1)][1];
+        lds_wait<2 * later>(f0, f1);
+        const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
+      });
     }
     // the next block's scores: mask and max while the P.V MFMAs run
     if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_cur);
     j_cur = j_n1;
     j_n1 = j_n2;
     j_n2 = j_n3;
+    if constexpr (QK8) ks_cur = ks_nxt;
   };
 
   for (int it = 0; it < cnt; it += 2) {
@@ -498,7 +584,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   }
 
   // epilogue: O = acc / l, this lane's query row, columns 32dt + 8g + 4hf + 0..3
-  const float lt = l_acc + __shfl_xor(l_acc, 32, 64);
+  const float lt = l_acc + partner32(l_acc, hf);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     char* ob = (char*)p.o;
