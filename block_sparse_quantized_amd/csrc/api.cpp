@@ -167,7 +167,7 @@ sparge_status prepare_operands(Ctx& c, const sparge_tensor* q, const sparge_tens
 }
 
 sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out,
-                            const sparge_opts& o, int causal, int filter_on) {
+                            const sparge_opts& o, int causal, int filter_on, bool k_ready = false) {
   AttnParams p{};
   p.q = op.q;
   p.k = op.k;
@@ -193,8 +193,9 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
     int8_t* k8 = c.at<int8_t>(c.w.k8);
     float* ks = c.at<float>(c.w.kscale);
     float* kb = c.at<float>(c.w.kbar);
-    SPARGE_TRY(launch_quant_k(op.k, op.dtype16, c.d, k8, c.d.D, (int64_t)c.d.nK * 64 * c.d.D, ks,
-                              kb, c.s));
+    if (!k_ready)
+      SPARGE_TRY(launch_quant_k(op.k, op.dtype16, c.d, k8, c.d.D, (int64_t)c.d.nK * 64 * c.d.D, ks,
+                                kb, c.s));
     p.k8 = k8;
     p.kscale = ks;
     p.kbar = kb;
@@ -217,6 +218,46 @@ sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor*
   SPARGE_TRY(launch_pooled_scores(qsum, ksum, c.d, causal, scale, scores, c.s));
   SPARGE_TRY(launch_select(scores, qsim, ksim, c.d, causal, topk, o.sim_threshold, mask_out,
                            c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts), c.counters, c.s));
+  return SPARGE_OK;
+}
+
+// 16-bit inputs: one fused pass over Q, K and V writes the predictor's block
+// statistics, the int8 K when asked for, and the fp16 V when the P.V type differs
+// from the input's; the operands then point at the inputs or at those copies.
+sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
+                     const sparge_tensor* v, const sparge_opts& o, Operands& op) {
+  const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
+  op.q = view_of(q);
+  op.k = view_of(k);
+  op.in_f16 = q->dtype == SPARGE_F16;
+  op.dtype16 = q->dtype;
+  const int v_f16 = o.pv_fp16 ? 1 : op.in_f16;
+  const int v_native = (v->dtype == SPARGE_F16 && v_f16) || (v->dtype == SPARGE_BF16 && !v_f16);
+  uint16_t* v16 = nullptr;
+  if (v_native) {
+    op.v = view_of(v);
+  } else {
+    v16 = c.at<uint16_t>(c.w.conv) + 2 * one;
+    op.v = View{v16, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
+  }
+  const int64_t chead = (int64_t)c.d.nK * 64 * c.d.D;
+  SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(v), q->dtype, c.d, c.at<double>(c.w.qsum),
+                         c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+                         o.qk_int8 ? c.at<int8_t>(c.w.k8) : nullptr, chead,
+                         (int64_t)c.d.nK * 64, c.at<float>(c.w.kscale), c.at<float>(c.w.kbar),
+                         v16, c.s));
+  return SPARGE_OK;
+}
+
+// Pooled scores and selection from the block statistics already in the workspace.
+sparge_status run_select(Ctx& c, double topk, int causal, const sparge_opts& o) {
+  const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
+  double* scores = c.at<double>(c.w.scores);
+  SPARGE_TRY(launch_pooled_scores(c.at<double>(c.w.qsum), c.at<double>(c.w.ksum), c.d, causal,
+                                  scale, scores, c.s));
+  SPARGE_TRY(launch_select(scores, c.at<double>(c.w.qsim), c.at<double>(c.w.ksim), c.d, causal,
+                           topk, o.sim_threshold, o.mask_out, c.at<uint16_t>(c.w.lists),
+                           c.at<int>(c.w.counts), c.counters, c.s));
   return SPARGE_OK;
 }
 
@@ -270,6 +311,12 @@ sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   Operands op;
+  if (q->dtype != SPARGE_F32) {
+    if ((st = prep16(c, q, k, v, o, op)) != SPARGE_OK) return st;
+    if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
+    if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0, true)) != SPARGE_OK) return st;
+    return end_stats(c, &o);
+  }
   if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) return st;
   if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
   if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0)) != SPARGE_OK) return st;
@@ -294,10 +341,18 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   Operands op;
-  if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) return st;
+  bool k_ready = false;
+  const int v_conv = v->dtype == SPARGE_BF16 && o.pv_fp16;
+  if (q->dtype != SPARGE_F32 && (o.qk_int8 || v_conv)) {
+    // the int8 K and the fp16 V in one pass (its block statistics go unused)
+    if ((st = prep16(c, q, k, v, o, op)) != SPARGE_OK) return st;
+    k_ready = true;
+  } else if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) {
+    return st;
+  }
   SPARGE_TRY(launch_compact(mask_id, c.d, c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts),
                             c.counters, c.s));
-  if ((st = run_attention(c, op, out, o, 0, o.filter_on != 0)) != SPARGE_OK) return st;
+  if ((st = run_attention(c, op, out, o, 0, o.filter_on != 0, k_ready)) != SPARGE_OK) return st;
   return end_stats(c, &o);
 }
 
@@ -314,6 +369,15 @@ sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  if (q->dtype != SPARGE_F32) {
+    // the statistics of the fused pass the attention path uses (no int8 K, no V)
+    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), q->dtype, c.d, c.at<double>(c.w.qsum),
+                           c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+                           nullptr, 0, 0, nullptr, nullptr, nullptr, c.s));
+    o.mask_out = mask_out;
+    if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
+    return end_stats(c, &o);
+  }
   if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, mask_out)) != SPARGE_OK) return st;
   return end_stats(c, &o);
 }
@@ -327,8 +391,15 @@ sparge_status sparge_quantize_qk(const sparge_tensor* q, const sparge_tensor* k,
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   SPARGE_TRY(launch_quant_q(view_of(q), q->dtype, c.d, q_codes, q_scales, c.s));
-  SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,
-                            k_scales, k_means, c.s));
+  if (k->dtype != SPARGE_F32) {
+    // the fused pass the attention path uses (its block statistics go unused)
+    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), k->dtype, c.d, c.at<double>(c.w.qsum),
+                           c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+                           k_codes, (int64_t)c.d.N * c.d.D, c.d.N, k_scales, k_means, nullptr, c.s));
+  } else {
+    SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,
+                              k_scales, k_means, c.s));
+  }
   return SPARGE_OK;
 }
 

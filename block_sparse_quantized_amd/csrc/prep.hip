@@ -1,0 +1,319 @@
+// Fused preparation pass of the top-k path on gfx950: one read of Q, K and V
+// produces everything the predictor and the attention kernel need before the
+// pooled scores.
+//
+//   * Q blocks (128 rows) and K blocks (64 rows): channel sums in fp64 and the
+//     block self-similarity || sum_r x_r/||x_r|| ||^2 / n^2 ([chapterpal] method
+//     paragraph: blocks with high internal similarity are compressed to their mean;
+//     [topgit] "Key features": 128 x 64 blocks);
+//   * optionally the block-smoothed int8 K of the SageAttention base ([topgit]
+//     "Key features"; [readme] "Avalible API"): kbar_j = fp32(fp64 row sum / rows),
+//     k'' = fp32(k) - kbar_j, a = max|k''| over the block, codes =
+//     clamp(rint(k'' * (127 / a)), -127, 127), step a / 127, all in IEEE fp32;
+//   * optionally V rounded (to nearest even) from bf16 to fp16 for the fp16 P.V.
+//
+// One workgroup of 256 threads per (b, h, Q block i): Q rows 128i..128i+127, the
+// K blocks 2i and 2i+1 over the same rows, and the same V rows.  Every 16-byte
+// chunk of the three tiles is loaded once, up front (coalesced: sixteen (D=128)
+// or eight (D=64) consecutive lanes read one row), and kept in registers.  Row
+// norms come from the registers (lane partials, then a reduction across the
+// row's lanes); the channel pass reads a copy of the tile in LDS (row pitch
+// padded by 16 bytes); the int8 codes come from the registers again and leave
+// as 8-byte stores.
+#include "sparge_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace sparge {
+namespace {
+
+constexpr int kPad = 16;  // bytes of padding per LDS tile row
+
+__device__ __forceinline__ float u16_to_f32(unsigned short u, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(_Float16, u) : __uint_as_float((unsigned int)u << 16);
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(b & 0xffffffffll), m, 64);
+  const int hi = __shfl_xor((int)(b >> 32), m, 64);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ signed char quant_code(float x, float inv) {
+  float c = __builtin_rintf(x * inv);
+  c = fminf(fmaxf(c, -127.0f), 127.0f);
+  return (signed char)(int)c;
+}
+
+template <int DT, int D, bool QUANT, bool VCONV>
+__global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims d, double* qsum,
+                                                   double* qsim, double* ksum, double* ksim,
+                                                   int8_t* codes, int64_t codes_head_stride,
+                                                   int64_t codes_rows, float* kscale, float* kbar,
+                                                   uint16_t* v16) {
+  constexpr bool F16 = DT == kF16;
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int NCH = 128 * CH / 256;     // chunks per thread
+  constexpr int ROWB = 2 * D + kPad;      // LDS bytes per tile row
+  constexpr int TPC = 256 / D;            // threads per channel in the channel pass
+  __shared__ __attribute__((aligned(16))) unsigned char tile[128 * ROWB];
+  __shared__ double inv_s[128];
+  __shared__ double part_s[256], part_u[256];
+  __shared__ double sq_s[4];
+  __shared__ float mean_s[2][D];
+  __shared__ float amax_s[4][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bh = blockIdx.x / d.nQ, i = blockIdx.x - bh * d.nQ;
+  const int b = bh / d.H, h = bh - b * d.H;
+  const int N = d.N;
+  const int r0 = 128 * i;
+  const int nrows = min(128, N - r0);
+
+  // every chunk of the three tiles, issued before any arithmetic
+  uint4 qr[NCH], kr[NCH], vr[NCH];
+  const unsigned short* qb = (const unsigned short*)q.p + (int64_t)b * q.sB + (int64_t)h * q.sH;
+  const unsigned short* kb = (const unsigned short*)k.p + (int64_t)b * k.sB + (int64_t)h * k.sH;
+  const unsigned short* vb = (const unsigned short*)v.p + (int64_t)b * v.sB + (int64_t)h * v.sH;
+#pragma unroll
+  for (int kk = 0; kk < NCH; ++kk) {
+    const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+    const bool ok = row < nrows;
+    const int64_t rr = r0 + row;
+    qr[kk] = ok ? *(const uint4*)(qb + rr * q.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
+    kr[kk] = ok ? *(const uint4*)(kb + rr * k.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
+    if constexpr (VCONV) vr[kk] = ok ? *(const uint4*)(vb + rr * v.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
+  }
+
+  // V: fp16 copy, rows < N only
+  if constexpr (VCONV) {
+#pragma unroll
+    for (int kk = 0; kk < NCH; ++kk) {
+      const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+      if (row < nrows) {
+        const unsigned int wd[4] = {vr[kk].x, vr[kk].y, vr[kk].z, vr[kk].w};
+        unsigned int o[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const _Float16 lo = (_Float16)u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16);
+          const _Float16 hi = (_Float16)u16_to_f32((unsigned short)(wd[c] >> 16), F16);
+          o[c] = (unsigned int)__builtin_bit_cast(unsigned short, lo) |
+                 ((unsigned int)__builtin_bit_cast(unsigned short, hi) << 16);
+        }
+        *(uint4*)(v16 + ((int64_t)bh * N + r0 + row) * D + 8 * ch) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+
+  // Row norms of the tile held in x[] (1/||x_r||, 0 for a zero row) into inv_s, and
+  // the tile into LDS.
+  auto stage = [&](const uint4 (&x)[NCH]) {
+#pragma unroll
+    for (int kk = 0; kk < NCH; ++kk) {
+      const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+      const unsigned int wd[4] = {x[kk].x, x[kk].y, x[kk].z, x[kk].w};
+      double ss = 0.0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double lo = u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16);
+        const double hi = u16_to_f32((unsigned short)(wd[c] >> 16), F16);
+        ss = ss + lo * lo;
+        ss = ss + hi * hi;
+      }
+#pragma unroll
+      for (int m = 1; m < CH; m <<= 1) ss = ss + shfl_xor_f64(ss, m);
+      if (ch == 0) {
+        const double nrm = sqrt(ss);
+        inv_s[row] = nrm > 0.0 ? 1.0 / nrm : 0.0;
+      }
+      *(uint4*)(tile + row * ROWB + 16 * ch) = x[kk];
+    }
+  };
+  // Channel sums s and unit-row sums u of tile rows [lo, hi) for this thread's
+  // channel, in row order.
+  auto channel_pass = [&](int c, int lo, int hi, double& s, double& u) {
+    s = 0.0;
+    u = 0.0;
+    for (int r = lo; r < hi; ++r) {
+      const double x = u16_to_f32(*(const unsigned short*)(tile + r * ROWB + 2 * c), F16);
+      s = s + x;
+      u = u + x * inv_s[r];
+    }
+  };
+
+  // ---- Q block i
+  stage(qr);
+  __syncthreads();
+  {
+    constexpr int RPP = 128 / TPC;
+    const int c = tid % D, part = tid / D;
+    double s, u;
+    channel_pass(c, part * RPP, min(part * RPP + RPP, nrows), s, u);
+    part_s[tid] = s;
+    part_u[tid] = u;
+    __syncthreads();
+    double sq = 0.0;
+    if (tid < D) {
+      double S = 0.0, U = 0.0;
+#pragma unroll
+      for (int pp = 0; pp < TPC; ++pp) {
+        S = S + part_s[pp * D + tid];
+        U = U + part_u[pp * D + tid];
+      }
+      qsum[((int64_t)bh * d.nQ + i) * D + tid] = S;
+      sq = U * U;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sq = sq + shfl_xor_f64(sq, m);
+    if (lane == 0) sq_s[wv] = sq;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w2 = 0; w2 < D / 64; ++w2) t = t + sq_s[w2];
+      qsim[(int64_t)bh * d.nQ + i] = t / (double)(nrows * nrows);
+    }
+  }
+  __syncthreads();  // the tile and inv_s are reused for K
+
+  // ---- K blocks 2i and 2i+1
+  stage(kr);
+  __syncthreads();
+  int nb[2];
+  nb[0] = min(64, nrows);
+  nb[1] = max(0, nrows - 64);
+  {
+    constexpr int PPB = TPC / 2;          // threads per (block, channel)
+    constexpr int RPP = 64 / PPB;
+    const int c = tid % D, part = tid / D;  // part in [0, TPC): block part / PPB
+    const int blk = part / PPB, sub = part % PPB;
+    double s, u;
+    channel_pass(c, 64 * blk + sub * RPP, 64 * blk + min(sub * RPP + RPP, nb[blk]), s, u);
+    part_s[tid] = s;
+    part_u[tid] = u;
+    __syncthreads();
+    // thread t < 2D finalizes (block t / D, channel t % D)
+    double sq = 0.0;
+    if (tid < 2 * D) {
+      const int fb = tid / D, fc = tid % D;
+      double S = 0.0, U = 0.0;
+#pragma unroll
+      for (int pp = 0; pp < PPB; ++pp) {
+        S = S + part_s[(fb * PPB + pp) * D + fc];
+        U = U + part_u[(fb * PPB + pp) * D + fc];
+      }
+      const int j = 2 * i + fb;
+      if (nb[fb] > 0) {
+        ksum[((int64_t)bh * d.nK + j) * D + fc] = S;
+        const float mean = (float)(S / (double)nb[fb]);
+        mean_s[fb][fc] = mean;
+        if constexpr (QUANT) kbar[((int64_t)bh * d.nK + j) * D + fc] = mean;
+      }
+      sq = U * U;
+    }
+    // 2D threads = (2D/64) waves; the first half of them hold block 0
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sq = sq + shfl_xor_f64(sq, m);
+    if (lane == 0) sq_s[wv] = sq;
+    __syncthreads();
+    if (tid < 2) {
+      constexpr int WPB = D / 64;  // waves per block in the finalize step
+      double t = 0.0;
+      for (int w2 = 0; w2 < WPB; ++w2) t = t + sq_s[tid * WPB + w2];
+      if (nb[tid] > 0) ksim[(int64_t)bh * d.nK + 2 * i + tid] = t / (double)(nb[tid] * nb[tid]);
+    }
+  }
+
+  if constexpr (QUANT) {
+    // max |k - kbar| per block over this thread's chunks, then over the workgroup
+    float am[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NCH; ++kk) {
+      const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+      if (row < nrows) {
+        const int blk = row >> 6;
+        const unsigned int wd[4] = {kr[kk].x, kr[kk].y, kr[kk].z, kr[kk].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float lo = u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16) - mean_s[blk][8 * ch + 2 * c];
+          const float hi = u16_to_f32((unsigned short)(wd[c] >> 16), F16) - mean_s[blk][8 * ch + 2 * c + 1];
+          am[blk] = fmaxf(am[blk], fmaxf(fabsf(lo), fabsf(hi)));
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      am[0] = fmaxf(am[0], __shfl_xor(am[0], m, 64));
+      am[1] = fmaxf(am[1], __shfl_xor(am[1], m, 64));
+    }
+    if (lane == 0) {
+      amax_s[wv][0] = am[0];
+      amax_s[wv][1] = am[1];
+    }
+    __syncthreads();
+    float a[2], inv[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      a[blk] = fmaxf(fmaxf(amax_s[0][blk], amax_s[1][blk]), fmaxf(amax_s[2][blk], amax_s[3][blk]));
+      inv[blk] = a[blk] > 0.0f ? 127.0f / a[blk] : 0.0f;
+    }
+    if (tid < 2 && nb[tid] > 0) kscale[(int64_t)bh * d.nK + 2 * i + tid] = a[tid] > 0.0f ? a[tid] / 127.0f : 0.0f;
+    // codes of every allocated row of the existing blocks (rows past N hold zeros)
+    int8_t* cb = codes + (int64_t)bh * codes_head_stride;
+#pragma unroll
+    for (int kk = 0; kk < NCH; ++kk) {
+      const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+      const int blk = row >> 6;
+      if (nb[blk] > 0 && r0 + row < codes_rows) {
+        unsigned int packed[2] = {0u, 0u};
+        if (row < nrows && a[blk] > 0.0f) {
+          const unsigned int wd[4] = {kr[kk].x, kr[kk].y, kr[kk].z, kr[kk].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float lo = u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16) - mean_s[blk][8 * ch + 2 * c];
+            const float hi = u16_to_f32((unsigned short)(wd[c] >> 16), F16) - mean_s[blk][8 * ch + 2 * c + 1];
+            const unsigned int pair = (unsigned int)(unsigned char)quant_code(lo, inv[blk]) |
+                                      ((unsigned int)(unsigned char)quant_code(hi, inv[blk]) << 8);
+            packed[c >> 1] |= pair << (16 * (c & 1));
+          }
+        }
+        *(uint2*)(cb + (int64_t)(r0 + row) * D + 8 * ch) = make_uint2(packed[0], packed[1]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
+                       double* qsum, double* qsim, double* ksum, double* ksim, int8_t* codes,
+                       int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
+                       uint16_t* v16, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
+  const bool quant = codes != nullptr, vconv = v16 != nullptr;
+#define SPARGE_PREP(DTV, DV, QV, VV)                                                             \
+  prep_kernel<DTV, DV, QV, VV><<<grid, 256, 0, s>>>(q, k, v, d, qsum, qsim, ksum, ksim, codes, \
+                                                    codes_head_stride, codes_rows, kscale, kbar, v16)
+#define SPARGE_PREP_D(DTV, DV)                                     \
+  do {                                                             \
+    if (quant) {                                                   \
+      if (vconv) SPARGE_PREP(DTV, DV, true, true);                 \
+      else SPARGE_PREP(DTV, DV, true, false);                      \
+    } else {                                                       \
+      if (vconv) SPARGE_PREP(DTV, DV, false, true);                \
+      else SPARGE_PREP(DTV, DV, false, false);                     \
+    }                                                              \
+  } while (0)
+  if (dtype == kF16) {
+    if (d.D == 64) SPARGE_PREP_D(kF16, 64);
+    else SPARGE_PREP_D(kF16, 128);
+  } else {
+    if (d.D == 64) SPARGE_PREP_D(kBF16, 64);
+    else SPARGE_PREP_D(kBF16, 128);
+  }
+#undef SPARGE_PREP_D
+#undef SPARGE_PREP
+  return hipGetLastError();
+}
+
+}  // namespace sparge

@@ -85,6 +85,16 @@ hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes
                           int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,
                           float* kbar, hipStream_t s);
 
+// Fused pass over 16-bit Q, K, V (one workgroup per Q block): the block sums and
+// self-similarities of launch_block_stats, plus, when codes != nullptr, the
+// block-smoothed int8 K of launch_quant_k (codes with D bytes per row, rows below
+// codes_rows written, those past N as zeros), and, when v16 != nullptr, V rounded
+// to fp16 into a contiguous (B, H, N, D) buffer.
+hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
+                       double* qsum, double* qsim, double* ksum, double* ksim, int8_t* codes,
+                       int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
+                       uint16_t* v16, hipStream_t s);
+
 // int8 Q codes with one step per 32 rows (the kernel the attention kernel mirrors).
 hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
                           hipStream_t s);

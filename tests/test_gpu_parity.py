@@ -231,7 +231,8 @@ def test_filter_skips_match_oracle(dev, causal):
 # -------------------------------------------------------------------- int8 path
 
 @pytest.mark.parametrize("dtype,N,D", [(torch.bfloat16, 1000, 128), (torch.float32, 333, 64),
-                                       (torch.float16, 64, 64)])
+                                       (torch.float16, 64, 64), (torch.bfloat16, 700, 64),
+                                       (torch.float16, 1000, 128)])
 def test_int8_codes_bit_exact(dev, dtype, N, D):
     wl = synth.workload("llm8k", H=3, N=N, D=D, dtype=dtype)
     q, k, _ = synth.make_qkv(wl, device=dev)
