@@ -18,9 +18,9 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   const size_t BH = (size_t)d.B * d.H;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
-  w.qsum = take(BH * d.nQ * d.D * sizeof(double));
+  w.qmean = take(BH * d.nQ * d.D * sizeof(double));
   w.qsim = take(BH * d.nQ * sizeof(double));
-  w.ksum = take(BH * d.nK * d.D * sizeof(double));
+  w.kmean = take(BH * d.nK * d.D * sizeof(double));
   w.ksim = take(BH * d.nK * sizeof(double));
   w.scores = take(BH * d.nQ * d.nK * sizeof(double));
   w.lists = take(BH * d.nQ * d.lstride * sizeof(uint16_t));
@@ -209,13 +209,13 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
 sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor* k, double topk,
                             int causal, const sparge_opts& o, uint8_t* mask_out) {
   const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
-  double* qsum = c.at<double>(c.w.qsum);
+  double* qmean = c.at<double>(c.w.qmean);
   double* qsim = c.at<double>(c.w.qsim);
-  double* ksum = c.at<double>(c.w.ksum);
+  double* kmean = c.at<double>(c.w.kmean);
   double* ksim = c.at<double>(c.w.ksim);
   double* scores = c.at<double>(c.w.scores);
-  SPARGE_TRY(launch_block_stats(view_of(q), view_of(k), q->dtype, c.d, qsum, qsim, ksum, ksim, c.s));
-  SPARGE_TRY(launch_pooled_scores(qsum, ksum, c.d, causal, scale, scores, c.s));
+  SPARGE_TRY(launch_block_stats(view_of(q), view_of(k), q->dtype, c.d, qmean, qsim, kmean, ksim, c.s));
+  SPARGE_TRY(launch_pooled_scores(qmean, kmean, c.d, causal, scale, scores, c.s));
   SPARGE_TRY(launch_select(scores, qsim, ksim, c.d, causal, topk, o.sim_threshold, mask_out,
                            c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts), c.counters, c.s));
   return SPARGE_OK;
@@ -241,8 +241,8 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
     op.v = View{v16, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
   }
   const int64_t chead = (int64_t)c.d.nK * 64 * c.d.D;
-  SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(v), q->dtype, c.d, c.at<double>(c.w.qsum),
-                         c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+  SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(v), q->dtype, c.d, c.at<double>(c.w.qmean),
+                         c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                          o.qk_int8 ? c.at<int8_t>(c.w.k8) : nullptr, chead,
                          (int64_t)c.d.nK * 64, c.at<float>(c.w.kscale), c.at<float>(c.w.kbar),
                          v16, c.s));
@@ -253,7 +253,7 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
 sparge_status run_select(Ctx& c, double topk, int causal, const sparge_opts& o) {
   const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
   double* scores = c.at<double>(c.w.scores);
-  SPARGE_TRY(launch_pooled_scores(c.at<double>(c.w.qsum), c.at<double>(c.w.ksum), c.d, causal,
+  SPARGE_TRY(launch_pooled_scores(c.at<double>(c.w.qmean), c.at<double>(c.w.kmean), c.d, causal,
                                   scale, scores, c.s));
   SPARGE_TRY(launch_select(scores, c.at<double>(c.w.qsim), c.at<double>(c.w.ksim), c.d, causal,
                            topk, o.sim_threshold, o.mask_out, c.at<uint16_t>(c.w.lists),
@@ -371,8 +371,8 @@ sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   if (q->dtype != SPARGE_F32) {
     // the statistics of the fused pass the attention path uses (no int8 K, no V)
-    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), q->dtype, c.d, c.at<double>(c.w.qsum),
-                           c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), q->dtype, c.d, c.at<double>(c.w.qmean),
+                           c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                            nullptr, 0, 0, nullptr, nullptr, nullptr, c.s));
     o.mask_out = mask_out;
     if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
@@ -393,8 +393,8 @@ sparge_status sparge_quantize_qk(const sparge_tensor* q, const sparge_tensor* k,
   SPARGE_TRY(launch_quant_q(view_of(q), q->dtype, c.d, q_codes, q_scales, c.s));
   if (k->dtype != SPARGE_F32) {
     // the fused pass the attention path uses (its block statistics go unused)
-    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), k->dtype, c.d, c.at<double>(c.w.qsum),
-                           c.at<double>(c.w.qsim), c.at<double>(c.w.ksum), c.at<double>(c.w.ksim),
+    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), k->dtype, c.d, c.at<double>(c.w.qmean),
+                           c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                            k_codes, (int64_t)c.d.N * c.d.D, c.d.N, k_scales, k_means, nullptr, c.s));
   } else {
     SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,

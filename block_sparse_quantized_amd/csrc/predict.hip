@@ -47,10 +47,11 @@ __device__ __forceinline__ double ld(const void* base, int64_t idx) {
 
 // One wavefront per block: Q blocks (128 rows) then K blocks (64 rows) of each
 // (b, h).  Pass 1 (one row per lane) forms 1/||x_r||; pass 2 (channels across
-// lanes) accumulates the channel sums and the sum of unit rows in row order.
+// lanes) accumulates the channel sums and the sum of unit rows in row order; the
+// means are the sums over the row count in fp64.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void block_stats_kernel(View q, View k, Dims d, double* qsum,
-                                                          double* qsim, double* ksum,
+__global__ __launch_bounds__(256) void block_stats_kernel(View q, View k, Dims d, double* qmean,
+                                                          double* qsim, double* kmean,
                                                           double* ksim) {
   constexpr int CPL = D / 64;  // channels per lane in pass 2
   const int lane = threadIdx.x & 63;
@@ -116,73 +117,65 @@ __global__ __launch_bounds__(256) void block_stats_kernel(View q, View k, Dims d
       u[c] = u[c] + v * iv;
     }
   }
-  double* sums = isq ? qsum : ksum;
+  double* means = isq ? qmean : kmean;
   const int nb = isq ? d.nQ : d.nK;
-  double* out = sums + ((int64_t)bh * nb + blk) * D;
+  double* out = means + ((int64_t)bh * nb + blk) * D;
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    out[CPL * lane + c] = s[c];
+    out[CPL * lane + c] = s[c] / (double)n;
     sq = sq + u[c] * u[c];
   }
   sq = wave_sum_f64(sq);
   if (lane == 0) (isq ? qsim : ksim)[(int64_t)bh * nb + blk] = sq / (double)(n * n);
 }
 
-// Pooled scores, one 32 (i) x 64 (j) tile per workgroup of 256 threads; means are
-// formed from the sums (fp64 division) while staging through LDS in 32-channel
-// chunks.  Tiles holding no valid pair under causality are skipped.
+// Pooled scores, one 64 (i) x 64 (j) tile per workgroup of 256 threads, 4 x 4
+// scores per thread; the block means stage through LDS channel-major in 32-channel
+// chunks.  Each score is one fused multiply-add chain in channel order.  Tiles
+// holding no valid pair under causality are skipped.
 template <int D>
-__global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qsum, const double* ksum,
+__global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qmean, const double* kmean,
                                                             Dims d, int causal, double scale,
                                                             double* scores) {
   constexpr int DC = 32;
-  __shared__ double qm[32][DC + 1];
-  __shared__ double km[64][DC + 1];
-  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 32, bh = blockIdx.z;
-  if (causal && j0 > 2 * (i0 + 31) + 1) return;
+  __shared__ double qm[DC][64 + 1];
+  __shared__ double km[DC][64 + 1];
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
+  if (causal && j0 > 2 * (i0 + 63) + 1) return;
   const int tid = threadIdx.x;
-  const int ti = tid / 16, tj = tid % 16;
-  double acc[2][4];
+  const int ti = tid >> 4, tj = tid & 15;   // rows i0 + ti + 16a, columns j0 + tj + 16b
+  double acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
   for (int c0 = 0; c0 < D; c0 += DC) {
-    for (int e = tid; e < 32 * DC; e += 256) {
-      const int ri = e / DC, cc = e % DC, i = i0 + ri;
-      double v = 0.0;
-      if (i < d.nQ) {
-        const int n = min(kBQ, d.N - i * kBQ);
-        v = qsum[((int64_t)bh * d.nQ + i) * D + c0 + cc] / (double)n;
-      }
-      qm[ri][cc] = v;
-    }
-    for (int e = tid; e < 64 * DC; e += 256) {
-      const int rj = e / DC, cc = e % DC, j = j0 + rj;
-      double v = 0.0;
-      if (j < d.nK) {
-        const int n = min(kBK, d.N - j * kBK);
-        v = ksum[((int64_t)bh * d.nK + j) * D + c0 + cc] / (double)n;
-      }
-      km[rj][cc] = v;
+#pragma unroll
+    for (int e0 = 0; e0 < 64 * DC; e0 += 256) {
+      const int e = e0 + tid, r = e / DC, cc = e % DC;
+      const int i = i0 + r, j = j0 + r;
+      qm[cc][r] = i < d.nQ ? qmean[((int64_t)bh * d.nQ + i) * D + c0 + cc] : 0.0;
+      km[cc][r] = j < d.nK ? kmean[((int64_t)bh * d.nK + j) * D + c0 + cc] : 0.0;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 8
     for (int cc = 0; cc < DC; ++cc) {
-      const double a0 = qm[2 * ti][cc], a1 = qm[2 * ti + 1][cc];
+      double av[4], bv[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double bv = km[tj + 16 * c][cc];
-        acc[0][c] = fma(a0, bv, acc[0][c]);
-        acc[1][c] = fma(a1, bv, acc[1][c]);
-      }
+      for (int a = 0; a < 4; ++a) av[a] = qm[cc][ti + 16 * a];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = km[cc][tj + 16 * c];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int i = i0 + 2 * ti + a;
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ti + 16 * a;
     if (i >= d.nQ) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -208,85 +201,126 @@ __device__ __forceinline__ int keep_count(int C, double topk) {
   return kk > C ? C : kk;
 }
 
-// One wavefront per block row (b, h, i).  Candidate keys sit in LDS; the k-th
-// largest key is found exactly by an 8-pass radix select (8-bit digits from the
-// most significant, an LDS histogram per pass and a wavefront suffix scan), ties at
-// the threshold go to the lowest block indices, and the kept blocks are compacted
-// in ascending order with ballots.
-__global__ __launch_bounds__(64) void select_kernel(const double* scores, const double* qsim,
-                                                    const double* ksim, Dims d, int causal,
-                                                    double topk, double theta, uint8_t* mask_out,
-                                                    uint16_t* lists, int* counts,
-                                                    unsigned long long* counters) {
-  extern __shared__ unsigned long long keys[];  // nK entries
-  unsigned char* flags = (unsigned char*)(keys + d.nK);  // bit0 valid, bit1 similar-K
+// One workgroup of 256 threads per block row (b, h, i).  Thread t holds the keys
+// of blocks j = t + 256m in registers (all loads issued up front).  The k-th
+// largest candidate key is found exactly by a radix select over 8-bit digits from
+// the most significant (an LDS histogram per pass over the keys that still match
+// the prefix, a suffix scan by one wavefront), stopping early once a single key
+// matches.  Ties at the threshold go to the lowest block indices; the kept blocks
+// are written in ascending order (ballots, then a prefix over the four waves).
+constexpr int kSelMaxM = 16;  // keys per thread: nK <= 4096
+
+__global__ __launch_bounds__(256) void select_kernel(const double* scores, const double* qsim,
+                                                     const double* ksim, Dims d, int causal,
+                                                     double topk, double theta, uint8_t* mask_out,
+                                                     uint16_t* lists, int* counts,
+                                                     unsigned long long* counters) {
   __shared__ unsigned int hist[256];
-  const int lane = threadIdx.x;
+  __shared__ int sh_int[4][2];
+  __shared__ int sh_sel[2];
+  __shared__ unsigned long long sh_key;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.x;
   const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
   const int nK = d.nK;
+  const int mk = (nK + 255) >> 8;
   const int jv = causal ? min(nK, 2 * i + 2) : nK;
   const bool simq = qsim[row] >= theta;
   const double* srow = scores + row * nK;
   const double* ks = ksim + (int64_t)bh * nK;
-  int cand_local = 0;
-  for (int j = lane; j < nK; j += 64) {
-    const bool valid = j < jv;
-    const bool simk = ks[j] >= theta;
-    flags[j] = (unsigned char)((valid ? 1 : 0) | (simk ? 2 : 0));
-    keys[j] = (valid && simk) ? order_key(srow[j]) : 0ull;
-    cand_local += (valid && simk) ? 1 : 0;
+
+  unsigned long long key[kSelMaxM];
+  unsigned int validm = 0u, simkm = 0u;
+  double kv[kSelMaxM];
+#pragma unroll
+  for (int m = 0; m < kSelMaxM; ++m) {
+    const int j = tid + 256 * m;
+    kv[m] = (m < mk && j < nK) ? ks[j] : 0.0;
   }
+  double sv[kSelMaxM];
+#pragma unroll
+  for (int m = 0; m < kSelMaxM; ++m) {
+    const int j = tid + 256 * m;
+    const bool valid = m < mk && j < jv;
+    sv[m] = valid ? srow[j] : 0.0;
+    validm |= (valid ? 1u : 0u) << m;
+  }
+  int cand_local = 0;
+#pragma unroll
+  for (int m = 0; m < kSelMaxM; ++m) {
+    const int j = tid + 256 * m;
+    const bool simk = m < mk && j < nK && kv[m] >= theta;
+    simkm |= (simk ? 1u : 0u) << m;
+    const bool cand = ((validm >> m) & 1u) && simk;
+    key[m] = cand ? order_key(sv[m]) : 0ull;
+    cand_local += cand ? 1 : 0;
+  }
+  const unsigned int candm = validm & simkm;
   for (int off = 32; off >= 1; off >>= 1) cand_local += __shfl_xor(cand_local, off, 64);
-  const int C = cand_local;
+  if (lane == 0) sh_int[wv][0] = cand_local;
+  __syncthreads();
+  const int C = sh_int[0][0] + sh_int[1][0] + sh_int[2][0] + sh_int[3][0];
   const int kk = keep_count(C, topk);
-  const int jhi = (jv < nK) ? jv : nK;  // candidates only exist below jv
   unsigned long long T = 0ull, pmask = 0ull;
   int need = 0;
   if (kk > 0) {
     int krem = kk;  // rank still to be located among keys matching the prefix
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
-      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+      hist[tid] = 0u;
       __syncthreads();
-      for (int j = lane; j < jhi; j += 64) {
-        if (flags[j] == 3) {
-          const unsigned long long key = keys[j];
-          if ((key & pmask) == T) atomicAdd(&hist[(unsigned int)(key >> shift) & 255u], 1u);
+#pragma unroll
+      for (int m = 0; m < kSelMaxM; ++m)
+        if (((candm >> m) & 1u) && (key[m] & pmask) == T)
+          atomicAdd(&hist[(unsigned int)(key[m] >> shift) & 255u], 1u);
+      __syncthreads();
+      if (wv == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending); suffix counts by scan
+        unsigned int c[4], tot = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = hist[255 - (4 * lane + e)];
+          tot += c[e];
+        }
+        unsigned int incl = tot;
+        for (int off = 1; off < 64; off <<= 1) {
+          const unsigned int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        unsigned int run = incl - tot;  // keys with a larger digit than this lane's range
+        int found = -1;
+        unsigned int above = 0u, here = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (found < 0 && run + c[e] >= (unsigned int)krem) {
+            found = 255 - (4 * lane + e);
+            above = run;
+            here = c[e];
+          }
+          run += c[e];
+        }
+        const unsigned long long fm = __ballot(found >= 0);
+        const int src = __ffsll((long long)fm) - 1;
+        if (lane == src) {
+          sh_sel[0] = found;
+          sh_sel[1] = (int)above;
+          sh_int[0][1] = (int)here;  // keys matching the extended prefix
         }
       }
       __syncthreads();
-      // lane l owns digits 255-4l .. 252-4l (descending); suffix counts by scan
-      unsigned int c[4], tot = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = hist[255 - (4 * lane + e)];
-        tot += c[e];
-      }
-      unsigned int incl = tot;
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      unsigned int run = incl - tot;  // keys with a larger digit than this lane's range
-      int found = -1;
-      unsigned int above = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (found < 0 && run + c[e] >= (unsigned int)krem) {
-          found = 255 - (4 * lane + e);
-          above = run;
-        }
-        run += c[e];
-      }
-      const unsigned long long fm = __ballot(found >= 0);
-      const int src = __ffsll((long long)fm) - 1;
-      const int dsel = __shfl(found, src, 64);
-      const unsigned int abv = __shfl(above, src, 64);
-      T |= (unsigned long long)dsel << shift;
+      T |= (unsigned long long)sh_sel[0] << shift;
       pmask |= 255ull << shift;
-      krem -= (int)abv;
-      __syncthreads();
+      krem -= sh_sel[1];
+      if (sh_int[0][1] == 1 && pass < 7) {
+        // a single key matches: it is the threshold
+#pragma unroll
+        for (int m = 0; m < kSelMaxM; ++m)
+          if (((candm >> m) & 1u) && (key[m] & pmask) == T) sh_key = key[m];
+        __syncthreads();
+        T = sh_key;
+        break;
+      }
+      __syncthreads();  // hist and sh_sel are rewritten by the next pass
     }
     need = krem;  // keys equal to T still to take (lowest block index first)
   }
@@ -294,24 +328,48 @@ __global__ __launch_bounds__(64) void select_kernel(const double* scores, const 
   int eq_before = 0, base = 0;
   uint8_t* mrow = mask_out ? mask_out + row * nK : nullptr;
   uint16_t* lrow = lists + row * d.lstride;
-  for (int j0 = 0; j0 < nK; j0 += 64) {
-    const int j = j0 + lane;
-    const unsigned f = j < nK ? flags[j] : 0u;
-    const bool valid = (f & 1u) != 0, simk = (f & 2u) != 0;
-    const bool cand = valid && simk;
-    const unsigned long long key = j < nK ? keys[j] : 0ull;
-    const bool is_eq = cand && kk > 0 && key == T;
-    const unsigned long long eqm = __ballot(is_eq);
-    const int rank = eq_before + __popcll(eqm & lt_mask);
-    eq_before += __popcll(eqm);
-    const bool sel = cand && kk > 0 && (key > T || (is_eq && rank < need));
-    const bool keep = valid && (!simq || !simk || sel);
-    if (mrow && j < nK) mrow[j] = keep ? 1 : 0;
-    const unsigned long long km = __ballot(keep);
-    if (keep) lrow[base + __popcll(km & lt_mask)] = (uint16_t)j;
-    base += __popcll(km);
+#pragma unroll
+  for (int m = 0; m < kSelMaxM; ++m) {
+    if (m < mk) {
+      const int j = tid + 256 * m;
+      const bool valid = (validm >> m) & 1u, simk = (simkm >> m) & 1u;
+      const bool cand = valid && simk;
+      const bool is_eq = cand && kk > 0 && key[m] == T;
+      const unsigned long long eqm = __ballot(is_eq);
+      const bool gt = cand && kk > 0 && key[m] > T;
+      const bool keep_pre = valid && (!simq || !simk || gt);
+      // ranks of the equal keys and positions of the kept blocks across the waves
+      if (lane == 0) {
+        sh_int[wv][0] = __popcll(eqm);
+      }
+      __syncthreads();
+      int eq_w = 0, eq_all = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int cw = sh_int[w2][0];
+        eq_w += (w2 < wv) ? cw : 0;
+        eq_all += cw;
+      }
+      const int rank = eq_before + eq_w + __popcll(eqm & lt_mask);
+      const bool keep = keep_pre || (is_eq && rank < need);
+      if (mrow && j < nK) mrow[j] = keep ? 1 : 0;
+      const unsigned long long km = __ballot(keep);
+      if (lane == 0) sh_int[wv][1] = __popcll(km);
+      __syncthreads();
+      int k_w = 0, k_all = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int cw = sh_int[w2][1];
+        k_w += (w2 < wv) ? cw : 0;
+        k_all += cw;
+      }
+      if (keep) lrow[base + k_w + __popcll(km & lt_mask)] = (uint16_t)j;
+      base += k_all;
+      eq_before += eq_all;
+      __syncthreads();  // sh_int is rewritten by the next chunk
+    }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     counts[row] = base;
     if (counters) {
       atomicAdd(&counters[0], (unsigned long long)jv);
@@ -385,12 +443,12 @@ __global__ __launch_bounds__(256) void convert16_kernel(View x, Dims d, uint16_t
 }  // namespace
 
 hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dims& d,
-                              double* qsum, double* qsim, double* ksum, double* ksim,
+                              double* qmean, double* qsim, double* kmean, double* ksim,
                               hipStream_t s) {
   const int64_t tasks = (int64_t)d.B * d.H * (d.nQ + d.nK);
   const dim3 grid((unsigned)((tasks + 3) / 4));
 #define SPARGE_STATS(DTV, DV) \
-  block_stats_kernel<DTV, DV><<<grid, 256, 0, s>>>(q, k, d, qsum, qsim, ksum, ksim)
+  block_stats_kernel<DTV, DV><<<grid, 256, 0, s>>>(q, k, d, qmean, qsim, kmean, ksim)
   if (d.D == 64) {
     if (dtype == kF32) SPARGE_STATS(kF32, 64);
     else if (dtype == kF16) SPARGE_STATS(kF16, 64);
@@ -404,14 +462,14 @@ hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dim
   return hipGetLastError();
 }
 
-hipError_t launch_pooled_scores(const double* qsum, const double* ksum, const Dims& d, int causal,
+hipError_t launch_pooled_scores(const double* qmean, const double* kmean, const Dims& d, int causal,
                                 double scale, double* scores, hipStream_t s) {
-  const dim3 grid((unsigned)((d.nK + 63) / 64), (unsigned)((d.nQ + 31) / 32),
+  const dim3 grid((unsigned)((d.nK + 63) / 64), (unsigned)((d.nQ + 63) / 64),
                   (unsigned)(d.B * d.H));
   if (d.D == 64)
-    pooled_scores_kernel<64><<<grid, 256, 0, s>>>(qsum, ksum, d, causal, scale, scores);
+    pooled_scores_kernel<64><<<grid, 256, 0, s>>>(qmean, kmean, d, causal, scale, scores);
   else
-    pooled_scores_kernel<128><<<grid, 256, 0, s>>>(qsum, ksum, d, causal, scale, scores);
+    pooled_scores_kernel<128><<<grid, 256, 0, s>>>(qmean, kmean, d, causal, scale, scores);
   return hipGetLastError();
 }
 
@@ -419,10 +477,10 @@ hipError_t launch_select(const double* scores, const double* qsim, const double*
                          const Dims& d, int causal, double topk, double theta, uint8_t* mask_out,
                          uint16_t* lists, int* counts, unsigned long long* counters,
                          hipStream_t s) {
-  const size_t lds = (size_t)d.nK * (sizeof(unsigned long long) + 1);
+  if (d.nK > 256 * kSelMaxM) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
-  select_kernel<<<grid, 64, lds, s>>>(scores, qsim, ksim, d, causal, topk, theta, mask_out, lists,
-                                      counts, counters);
+  select_kernel<<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, topk, theta, mask_out, lists,
+                                     counts, counters);
   return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
 // produces everything the predictor and the attention kernel need before the
 // pooled scores.
 //
-//   * Q blocks (128 rows) and K blocks (64 rows): channel sums in fp64 and the
+//   * Q blocks (128 rows) and K blocks (64 rows): channel means in fp64 and the
 //     block self-similarity || sum_r x_r/||x_r|| ||^2 / n^2 ([chapterpal] method
 //     paragraph: blocks with high internal similarity are compressed to their mean;
 //     [topgit] "Key features": 128 x 64 blocks);
@@ -47,8 +47,8 @@ __device__ __forceinline__ signed char quant_code(float x, float inv) {
 }
 
 template <int DT, int D, bool QUANT, bool VCONV>
-__global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims d, double* qsum,
-                                                   double* qsim, double* ksum, double* ksim,
+__global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims d, double* qmean,
+                                                   double* qsim, double* kmean, double* ksim,
                                                    int8_t* codes, int64_t codes_head_stride,
                                                    int64_t codes_rows, float* kscale, float* kbar,
                                                    uint16_t* v16) {
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
         S = S + part_s[pp * D + tid];
         U = U + part_u[pp * D + tid];
       }
-      qsum[((int64_t)bh * d.nQ + i) * D + tid] = S;
+      qmean[((int64_t)bh * d.nQ + i) * D + tid] = S / (double)nrows;
       sq = U * U;
     }
 #pragma unroll
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
       }
       const int j = 2 * i + fb;
       if (nb[fb] > 0) {
-        ksum[((int64_t)bh * d.nK + j) * D + fc] = S;
-        const float mean = (float)(S / (double)nb[fb]);
-        mean_s[fb][fc] = mean;
-        if constexpr (QUANT) kbar[((int64_t)bh * d.nK + j) * D + fc] = mean;
+        const double mean = S / (double)nb[fb];
+        kmean[((int64_t)bh * d.nK + j) * D + fc] = mean;
+        mean_s[fb][fc] = (float)mean;
+        if constexpr (QUANT) kbar[((int64_t)bh * d.nK + j) * D + fc] = (float)mean;
       }
       sq = U * U;
     }
@@ -286,13 +286,13 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
 }  // namespace
 
 hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
-                       double* qsum, double* qsim, double* ksum, double* ksim, int8_t* codes,
+                       double* qmean, double* qsim, double* kmean, double* ksim, int8_t* codes,
                        int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
                        uint16_t* v16, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
   const bool quant = codes != nullptr, vconv = v16 != nullptr;
 #define SPARGE_PREP(DTV, DV, QV, VV)                                                             \
-  prep_kernel<DTV, DV, QV, VV><<<grid, 256, 0, s>>>(q, k, v, d, qsum, qsim, ksum, ksim, codes, \
+  prep_kernel<DTV, DV, QV, VV><<<grid, 256, 0, s>>>(q, k, v, d, qmean, qsim, kmean, ksim, codes, \
                                                     codes_head_stride, codes_rows, kscale, kbar, v16)
 #define SPARGE_PREP_D(DTV, DV)                                     \
   do {                                                             \

@@ -40,7 +40,7 @@ inline Dims make_dims(int B, int H, int N, int D) {
 // Workspace: one buffer, carved into 256-byte aligned regions.
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t qsum, qsim, ksum, ksim;   // fp64 block sums and self-similarities
+  size_t qmean, qsim, kmean, ksim; // fp64 block means and self-similarities
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
   size_t lists, counts;            // uint16 kept-block lists (BH, nQ, lstride), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
@@ -60,14 +60,14 @@ Workspace plan_workspace(const Dims& d, int dtype);
 hipError_t launch_convert16(const View& x, int src_dtype, const Dims& d, uint16_t* dst,
                             int dst_f16, hipStream_t s);
 
-// Per block (Q: 128 rows, K: 64 rows) channel sums in fp64 and self-similarity.
+// Per block (Q: 128 rows, K: 64 rows) channel means in fp64 and self-similarity.
 hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dims& d,
-                              double* qsum, double* qsim, double* ksum, double* ksim,
+                              double* qmean, double* qsim, double* kmean, double* ksim,
                               hipStream_t s);
 
 // Pooled scores s_ij = scale * qbar_i . kbar_j (fp64) for every block pair that can
 // be valid.
-hipError_t launch_pooled_scores(const double* qsum, const double* ksum, const Dims& d,
+hipError_t launch_pooled_scores(const double* qmean, const double* kmean, const Dims& d,
                                 int causal, double scale, double* scores, hipStream_t s);
 
 // Per block row: similarity gate, top-k selection, mask row and kept-block list.
@@ -85,13 +85,13 @@ hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes
                           int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,
                           float* kbar, hipStream_t s);
 
-// Fused pass over 16-bit Q, K, V (one workgroup per Q block): the block sums and
+// Fused pass over 16-bit Q, K, V (one workgroup per Q block): the block means and
 // self-similarities of launch_block_stats, plus, when codes != nullptr, the
 // block-smoothed int8 K of launch_quant_k (codes with D bytes per row, rows below
 // codes_rows written, those past N as zeros), and, when v16 != nullptr, V rounded
 // to fp16 into a contiguous (B, H, N, D) buffer.
 hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
-                       double* qsum, double* qsim, double* ksum, double* ksim, int8_t* codes,
+                       double* qmean, double* qsim, double* kmean, double* ksim, int8_t* codes,
                        int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
                        uint16_t* v16, hipStream_t s);
 
