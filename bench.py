@@ -269,6 +269,37 @@ def sdpa_baseline(q, k, v, causal, steps=3):
         return None
 
 
+SWEEP_N = (8192, 16384, 32768, 65536, 131072)
+
+
+def sweep(wl, dev, ev, main_path, steps=3):
+    """Dense-equivalent TOPS and latency over N = 8K..128K (the LLM generator, causal,
+    topk 0.5, filter on), for the int8 Q.K^T / fp16 P.V path and the bf16 path."""
+    from block_sparse_quantized_amd import synth
+    out = []
+    for n in SWEEP_N:
+        wn = synth.workload("llm8k", N=n)
+        inputs = None
+        if n == main_path.wl.N and wl.B == main_path.wl.B and wl.H == main_path.wl.H:
+            inputs = (main_path.q, main_path.k, main_path.v, main_path.mask)
+        for qk8, pv16 in ((True, True), (False, False)):
+            pth = Path(wn, dev, qk_int8=qk8, pv_fp16=pv16, inputs=inputs)
+            inputs = (pth.q, pth.k, pth.v, pth.mask)
+            _, st = pth.step(stats=True)
+            s_ms, a_ms, _ = time_path(pth, ev, steps, 1)
+            dense = dense_equiv_ops(wn.B, wn.H, n, wn.D, wn.causal)
+            rf = roofline(st, wn.D, qk8, a_ms, None)
+            out.append({"N": n, "path": "i8-qk/f16-pv" if qk8 else "bf16",
+                        "ms_per_step": round(s_ms, 4), "attention_ms": round(a_ms, 4),
+                        "tops_dense_equiv": round(dense / (s_ms * 1e-3) / 1e12, 2),
+                        "attention_frac": rf["frac"], "attention_frac_of_bf16_peak": rf["frac_of_bf16_peak"],
+                        "kept_block_density": round(st["kept_blocks"] / max(1, st["valid_blocks"]), 4)})
+            log(f"[bench] sweep N={n} {out[-1]['path']}: {out[-1]['tops_dense_equiv']} TOPS, "
+                f"{s_ms:.3f} ms/step")
+            del pth
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +366,8 @@ def main():
             extras["dense_ours_bf16"] = {"ms_per_step": round(sd, 3),
                                          "tops_dense_equiv": round(dense / (sd * 1e-3) / 1e12, 2)}
             del pd
+        if wl.name in ("llm8k", "llm128k"):
+            extras["sweep"] = sweep(wl, dev, ev, path)
         ms_sdpa = sdpa_baseline(path.q, path.k, path.v, wl.causal)
         if ms_sdpa is not None:
             extras["dense_torch_sdpa_bf16"] = {"ms_per_step": round(ms_sdpa, 3),
