@@ -331,34 +331,46 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     const int r = (4 * cc + w) * (1024 / VROW) + lane / VG;
     voff[cc] = (unsigned int)(r * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
   }
+  // Block bases as 32 x 32 -> 64-bit products (row strides are below 4 GB); one
+  // wave-uniform branch per tile chooses the precomputed offsets (full block) or
+  // the clamped ones (the ragged last block).
+  const unsigned int ksrow32 = (unsigned int)ksrow, vsrow32 = (unsigned int)vsrow;
   auto dma_k = [&](int j, auto kstage) {
     unsigned char* dst = decltype(kstage)::value ? Ks1 : Ks0;
-    const char* base = Kb + (int64_t)(64 * j) * ksrow;
-    const bool full = QK8 || (64 * j + 64 <= N);
+    const char* base = Kb + (uint64_t)(unsigned int)(64 * j) * ksrow32;
+    if (QK8 || 64 * j + 64 <= N) {
 #pragma unroll
-    for (int cc = 0; cc < KCW; ++cc) {
-      const int c = 4 * cc + w;
-      unsigned int off = koff[cc];
-      if (!full) {
+      for (int cc = 0; cc < KCW; ++cc)
+        __builtin_amdgcn_global_load_lds((const void*)(base + koff[cc]),
+                                         (lds_void_ptr)(dst + 1024 * (4 * cc + w)), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < KCW; ++cc) {
+        const int c = 4 * cc + w;
         const int r = c * (1024 / KROW) + lane / KG;
-        off = (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+        const unsigned int off =
+            (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
     }
   };
   auto dma_v = [&](int j, auto vstage) {
     unsigned char* dst = decltype(vstage)::value ? Vs1 : Vs0;
-    const char* base = Vb + (int64_t)(64 * j) * vsrow;
-    const bool full = 64 * j + 64 <= N;
+    const char* base = Vb + (uint64_t)(unsigned int)(64 * j) * vsrow32;
+    if (64 * j + 64 <= N) {
 #pragma unroll
-    for (int cc = 0; cc < VCW; ++cc) {
-      const int c = 4 * cc + w;
-      unsigned int off = voff[cc];
-      if (!full) {
+      for (int cc = 0; cc < VCW; ++cc)
+        __builtin_amdgcn_global_load_lds((const void*)(base + voff[cc]),
+                                         (lds_void_ptr)(dst + 1024 * (4 * cc + w)), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < VCW; ++cc) {
+        const int c = 4 * cc + w;
         const int r = c * (1024 / VROW) + lane / VG;
-        off = (unsigned int)(min(r, N - 1 - 64 * j) * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+        const unsigned int off =
+            (unsigned int)(min(r, N - 1 - 64 * j) * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
     }
   };
 
@@ -428,6 +440,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   int j_cur = cnt > 0 ? list_at(0) : 0;   // block of step it
   int j_n1 = cnt > 1 ? list_at(1) : 0;    // block it+1
   int j_n2 = cnt > 2 ? list_at(2) : 0;    // block it+2
+  // The list as 32-bit words of two entries, one scalar load per two steps: at an
+  // even step it, lw holds entries it+2 and it+3 and the word of it+4 and it+5 is
+  // loaded for the next two steps.  Word indices are clamped into the row.
+  const int lw_last = (d.lstride >> 1) - 1;
+  unsigned int lw = lst32[min(1, lw_last)];
   acc_t acc_cur[2];
   f32x16 sc_cur[2];
   float mraw_cur = kNegInf;
@@ -442,12 +459,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     mraw_cur = mask_max(acc_cur, j_cur, sc_cur);
   }
 
+  unsigned int lw_nxt = 0u;
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;        // it & 1
     std::integral_constant<int, P> sp;
     std::integral_constant<int, 1 - P> sq;
     const int j = j_cur;
-    const int j_n3 = (it + 3 < cnt) ? list_at(it + 3) : 0;
+    int j_n3;
+    if constexpr (P == 0) {
+      j_n3 = (int)(lw >> 16);                              // entry it+3
+      lw_nxt = lst32[min((it >> 1) + 2, lw_last)];         // entries it+4, it+5
+    } else {
+      j_n3 = (int)(lw_nxt & 0xffffu);                      // entry it+3 (= it+4 of the even step)
+      lw = lw_nxt;
+    }
+    if (it + 3 >= cnt) j_n3 = 0;
     const float ks_nxt = QK8 ? kscale_at(j_n1) : 0.0f;   // K step of the next block
     wait_vmem_all();     // this wavefront's DMAs of K(it+1) and V(it) have landed
     __syncthreads();     // ... and every wavefront's; K stage P and V stage 1-P are free
