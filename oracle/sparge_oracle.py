@@ -469,3 +469,138 @@ def attend_head_int8_sim(q32, k32, v, mask_bh, causal, q_rows=Q_QUANT_ROWS, scal
             o[~nz] = 0
             out[g0:g1] = o
     return out
+
+
+# ---------------------------------------------------------------------------------
+# fp8 P.V option (the SageAttention2 base the pages name runs P.V in 8-bit floating
+# point; [readme] "Installation" lists fp8 support; [topgit] "Key features").
+# Readings (the pages give no formula):
+#   * format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+#     subnormals down to 2^-9, largest finite 448, no infinities); rounding to
+#     nearest, ties to even;
+#   * V: one fp32 scale per (head, channel) over the whole sequence,
+#     s_d = fp32(max_n |v_nd| / 448), and codes e4m3(fp32(v_nd * fp32(448 / max)));
+#     a channel that is all zero gets scale 0 and zero codes;
+#   * P: each softmax numerator, taken as 2^(z log2(e) - ceil(row max log2(e))) (so
+#     the largest lies in (1/2, 1]), rounded to E4M3; the normaliser is the sum of
+#     the ROUNDED numerators, so the weights of a row still sum to one;
+#   * O = (sum_n e4m3(P_n) * code_nd) * s_d / sum_n e4m3(P_n), accumulated in fp64.
+# ---------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+LOG2E = 1.0 / math.log(2.0)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP FP8 E4M3 value of each fp64 x (ties to even), as fp64.
+
+    Normal values have 3 fraction bits, so one unit in the last place is
+    2^(e - 3) for x in [2^e, 2^(e+1)); below 2^-6 the spacing stays 2^-9
+    (subnormals).  |x| above the largest finite value is outside the format; the
+    callers keep |x| <= 448, and this function raises rather than saturate."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e2 = np.frexp(a)                          # a = f * 2^e2, f in [0.5, 1)
+    ulp = np.ldexp(1.0, np.maximum(e2 - 4, -9))  # 2^(floor(log2 a) - 3), at least 2^-9
+    r = np.rint(a / ulp) * ulp                   # a / ulp < 16: exact; rint is ties-to-even
+    if np.any(r > E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    return np.copysign(r, x)
+
+
+def fp8_v_quant(v32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-channel E4M3 codes of V (as fp64 values) and the fp32 channel scales."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    vmax = np.abs(v32).max(axis=0)                                     # exact
+    with np.errstate(divide="ignore"):
+        inv = np.where(vmax > 0, np.float32(E4M3_MAX) / vmax, np.float32(0)).astype(np.float32)
+    scale = (vmax / np.float32(E4M3_MAX)).astype(np.float32)
+    codes = e4m3_round((v32 * inv[None, :]).astype(np.float32).astype(np.float64))
+    return codes, scale
+
+
+def _pv8_group(z_blocks, c_blocks, sv, G, D):
+    """O rows of one filter group from its logit blocks and E4M3 V code blocks."""
+    if not z_blocks:
+        return np.zeros((G, D))
+    Z = np.concatenate(z_blocks, axis=1)
+    C = np.concatenate(c_blocks, axis=0)
+    # P = 2^(z log2(e) - M) with M = ceil(row max * log2(e)): the row max lands in
+    # (1/2, 1], and any other integer M' >= M only multiplies every P by a power of
+    # two, which E4M3 rounding commutes with outside its subnormal range
+    m = Z.max(axis=1) * LOG2E
+    ok = np.isfinite(m)
+    M = np.where(ok, np.ceil(m), 0.0)
+    Pr = e4m3_round(np.exp2(Z * LOG2E - M[:, None]))
+    l = Pr.sum(axis=1)
+    o = (Pr @ C) * sv.astype(np.float64)[None, :]
+    out = np.zeros((G, D))
+    nz = l > 0
+    out[nz] = o[nz] / l[nz, None]
+    return out
+
+
+def attend_rows_pv8(q, k, v, mask_bh, groups, causal, scale=None, lam=None, group=32,
+                    qk: str = "exact", q_rows=Q_QUANT_ROWS) -> Dict[Tuple[int, int], np.ndarray]:
+    """Stage 2 with the fp8 P.V for the listed (block row i, group g) pairs.
+
+    V: per-channel E4M3 codes over the whole head (``fp8_v_quant``).  Logits: the
+    exact fp64 ones (qk="exact") or the int8 ones of ``attend_head_int8_sim``
+    (qk="int8").  The filter, when ``lam`` is set, runs on those logits as in
+    ``attend_group``.  Then P = 2^(z log2(e) - ceil(row max log2(e))) over the
+    remaining keys, rounded to E4M3, and O = (sum P~ code) * s / sum P~ in fp64.
+    Returns O rows in fp64."""
+    q32 = np.asarray(q, dtype=np.float32)
+    k32 = np.asarray(k, dtype=np.float32)
+    N, D = q32.shape
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    codes, sv = fp8_v_quant(v)
+    q64, k64 = q32.astype(np.float64), k32.astype(np.float64)
+    if qk == "int8":
+        qc, qd, kc, kd, kbar = int8_qk_inputs(q32, k32, q_rows)
+        qi, ki = qc.astype(np.int64), kc.astype(np.int64)
+        kbar64 = kbar.astype(np.float64)
+    res = {}
+    for (i, g) in groups:
+        g0 = BQ * i + group * g
+        g1 = min(N, g0 + group, BQ * i + BQ)
+        if g0 >= g1:
+            continue
+        t = np.arange(g0, g1)
+        zs, cs = [], []
+        m_run = np.full(g1 - g0, -np.inf)
+        for j in np.flatnonzero(mask_bh[i]):
+            s0, s1 = BK * j, min(N, BK * j + BK)
+            if qk == "int8":
+                dq = qd[t // q_rows].astype(np.float64)
+                z = scale * (dq[:, None] * np.float64(kd[j]) * (qi[g0:g1] @ ki[s0:s1].T).astype(np.float64)
+                             + (q64[g0:g1] @ kbar64[j])[:, None])
+            else:
+                z = scale * (q64[g0:g1] @ k64[s0:s1].T)
+            if causal:
+                z = np.where(np.arange(s0, s1)[None, :] <= t[:, None], z, -np.inf)
+            if lam is not None:
+                m_loc = z.max(axis=1)
+                m_new = np.maximum(m_run, m_loc)
+                fin = np.isfinite(m_loc)
+                if (not fin.any()) or (m_loc[fin] - m_new[fin]).max() < lam:
+                    continue
+                m_run = m_new
+            zs.append(z)
+            cs.append(codes[s0:s1])
+        res[(i, g)] = _pv8_group(zs, cs, sv, g1 - g0, D)
+    return res
+
+
+def attend_head_pv8_sim(q, k, v, mask_bh, causal, scale=None, lam=None, group=32,
+                        qk: str = "exact", q_rows=Q_QUANT_ROWS):
+    """``attend_rows_pv8`` over every row group of one head, as an (N, D) array."""
+    N = np.asarray(q).shape[0]
+    nQ = mask_bh.shape[0]
+    groups = [(i, g) for i in range(nQ) for g in range((BQ + group - 1) // group)]
+    res = attend_rows_pv8(q, k, v, mask_bh, groups, causal, scale, lam, group, qk, q_rows)
+    out = np.zeros((N, np.asarray(q).shape[1]))
+    for (i, g), o in res.items():
+        g0 = BQ * i + group * g
+        out[g0:g0 + o.shape[0]] = o
+    return out

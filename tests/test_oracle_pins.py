@@ -528,3 +528,144 @@ def test_int8_codes_are_integer_decisions_in_fp32():
         blk = q[32 * g: 32 * g + 32]
         assert np.abs(qc[32 * g: 32 * g + 32]).max() == 127
         assert qd[g] == np.float32(np.abs(blk).max()) / np.float32(127)
+
+
+# ------------------------------------------------------------------ fp8 P.V option
+
+def _e4m3_table():
+    """Every finite non-negative OCP E4M3 value, decoded from its bit fields (bias 7,
+    3 fraction bits, exponent field 0 = subnormal, code 0x7f = NaN); index = code."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def test_e4m3_fixed_points_and_range():
+    t = _e4m3_table()
+    assert len(t) == 127 and np.all(np.diff(t) > 0)
+    assert t[-1] == 448.0 and t[1] == 2.0 ** -9 and t[8] == 2.0 ** -6
+    assert np.array_equal(so.e4m3_round(t), t)
+    assert np.array_equal(so.e4m3_round(-t), -t)
+    assert so.e4m3_round(np.array([463.9]))[0] == 448.0      # below the 448/512 midpoint
+    with pytest.raises(ValueError):
+        so.e4m3_round(np.array([465.0]))
+
+
+def test_e4m3_nearest_with_ties_to_even_code():
+    t = _e4m3_table()
+    mids = (t[:-1] + t[1:]) / 2
+    want = np.where(np.arange(len(mids)) % 2 == 0, t[:-1], t[1:])   # even code wins
+    assert np.array_equal(so.e4m3_round(mids), want)
+    gap = t[1:] - t[:-1]
+    assert np.array_equal(so.e4m3_round(mids - 1e-3 * gap), t[:-1])
+    assert np.array_equal(so.e4m3_round(mids + 1e-3 * gap), t[1:])
+    r = np.random.default_rng(11)
+    x = np.concatenate([r.uniform(0, 448, 3000), np.exp2(r.uniform(-12, 8.8, 3000))])
+    x = x[x < 448]
+    near = t[np.abs(x[:, None] - t[None, :]).argmin(axis=1)]     # brute force
+    assert np.array_equal(so.e4m3_round(x), near)
+
+
+def test_e4m3_matches_torch_float8():
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch has no float8_e4m3fn")
+    r = np.random.default_rng(12)
+    x = np.exp2(r.uniform(-12, 8.8, 20000)) * r.choice([-1.0, 1.0], 20000)
+    x = np.concatenate([x[np.abs(x) < 448], (_e4m3_table()[:-1] + _e4m3_table()[1:]) / 2])
+    x32 = x.astype(np.float32)
+    lib = torch.from_numpy(x32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(so.e4m3_round(x32.astype(np.float64)), lib)
+
+
+def test_fp8_v_quant_grid_zero_channel_and_error_bound():
+    t = _e4m3_table()
+    r = np.random.default_rng(13)
+    codes = r.choice(t[8:], size=(200, 16)) * r.choice([-1.0, 1.0], size=(200, 16))
+    codes[7, :] = 448.0                                  # every channel reaches the max
+    v = codes * 0.125                                    # max |v| = 56 -> inv = 8 exactly
+    v[:, 3] = 0.0
+    c, s = so.fp8_v_quant(v)
+    assert s.dtype == np.float32 and s[3] == 0 and not c[:, 3].any()
+    keep = np.arange(16) != 3
+    assert np.all(s[keep] == np.float32(0.125))
+    assert np.array_equal(c[:, keep], codes[:, keep])
+    x = (r.standard_normal((500, 8)) * np.array([1e-3, 0.1, 1, 3, 10, 100, 1e4, 0.5])).astype(np.float32)
+    c, s = so.fp8_v_quant(x)
+    assert np.all(np.abs(c).max(axis=0) == 448.0)
+    y = x.astype(np.float64) * (np.float64(448.0) / np.abs(x.astype(np.float64)).max(axis=0))
+    # half a unit in the last place: 2^-4 relative for normals, 2^-10 absolute below 2^-6
+    assert np.all(np.abs(c - y) <= np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10) * (1 + 1e-5))
+
+
+def _pow2_logit_head(N, D, seed):
+    """q, k with scale-1 logits z = n ln 2 for integers n in [-6, 2] (so every
+    2^(z log2 e - M) is an exact E4M3 value) and V on the E4M3 grid times 1/8 with
+    every channel's max |v| = 56."""
+    r = np.random.default_rng(seed)
+    q = np.zeros((N, D))
+    q[:, 0] = math.log(2.0)
+    k = np.zeros((N, D))
+    k[:, 0] = r.integers(-6, 3, size=N)
+    t = _e4m3_table()
+    v = r.choice(t[8:], size=(N, D)) * r.choice([-1.0, 1.0], size=(N, D)) * 0.125
+    v[r.integers(0, N), :] = 56.0
+    return q, k, v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pv8_exact_when_p_and_v_are_representable(causal):
+    N, D = 300, 16
+    q, k, v = _pow2_logit_head(N, D, 14 + causal)
+    mask = so.block_valid(N, causal)
+    o8 = so.attend_head_pv8_sim(q, k, v, mask, causal, scale=1.0)
+    assert np.abs(o8 - sdpa64(q, k, v, causal=causal, scale=1.0)).max() < 1e-12
+    # the filter with lambda = -inf changes nothing
+    o8f = so.attend_head_pv8_sim(q, k, v, mask, causal, scale=1.0, lam=-np.inf)
+    assert np.array_equal(o8, o8f)
+
+
+def test_pv8_rounded_weights_closed_form():
+    # two keys with P = (1, 1.0625) relative to the max: 2^(z log2 e - 1) = (0.5, 0.53125),
+    # and 0.53125 is the midpoint of 0.5 and 0.5625, so E4M3 gives (0.5, 0.5) and
+    # O = (v0 + v1) / 2 exactly (normaliser over the rounded weights)
+    D = 8
+    q = np.zeros((2, D))
+    q[:, 0] = 1.0
+    k = np.zeros((2, D))
+    k[1, 0] = math.log(1.0625)
+    v = np.zeros((2, D))
+    v[0, :] = 56.0
+    v[1, :] = np.linspace(-56, 56, D) * 0.5
+    v[1, 0] = -56.0
+    o = so.attend_head_pv8_sim(q, k, v, np.ones((1, 1), bool), False, scale=1.0)
+    c, s = so.fp8_v_quant(v)
+    want = (c[0] + c[1]) * s.astype(np.float64) / 2
+    assert np.abs(o[0] - want).max() < 1e-12 and np.abs(o[1] - want).max() < 1e-12
+
+
+def test_pv8_close_to_exact_and_int8_variant():
+    N, D = 512, 64
+    q, k, v = _drift_head(N, D, 15)
+    mask = so.block_valid(N, True)
+    o = so.attend_head(q, k, v, mask, True)
+    o8 = so.attend_head_pv8_sim(q, k, v, mask, True)
+    o8i = so.attend_head_pv8_sim(q, k, v, mask, True, qk="int8")
+    vmax = np.abs(v).max()
+    c, s = so.fp8_v_quant(v)
+    verr = np.abs(c * s - v).max()
+    # a sanity bound: each value moves by at most verr and each normal weight by at
+    # most 2^-4 of itself (subnormal weights, below 2^-6 of the row max, by 2^-10)
+    assert 1e-4 < np.abs(o - o8).max() <= verr + 2 * 2.0 ** -4 / (1 - 2.0 ** -4) * 2 * vmax
+    assert np.abs(o8 - o8i).max() < 0.05 * vmax
+    # rows with many keys average the rounding errors out
+    assert np.abs(o - o8)[256:].mean() < 2e-3 * vmax
+
+
+def test_planted_unrounded_p_is_caught(monkeypatch):
+    monkeypatch.setattr(so, "e4m3_round", lambda x: np.asarray(x, dtype=np.float64))
+    with pytest.raises(AssertionError):
+        test_pv8_rounded_weights_closed_form()
