@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "dense-equiv TOPS & latency of sparse attn at N=8K..128K, topk=0.5; MFMA util"
 PEAK_BF16 = 2.5e15      # dense bf16/fp16 MFMA, FLOP/s (MI355X published)
 PEAK_INT8 = 5.0e15      # dense int8 MFMA, OP/s
+PEAK_FP8 = 5.0e15       # dense fp8 (E4M3) MFMA, MI355X published
 BK, BQ, G = 64, 128, 32
 
 
@@ -82,7 +83,7 @@ def dense_equiv_ops(B, H, N, D, causal):
 class Path:
     """The hot path of one workload with preallocated outputs and workspace."""
 
-    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None):
+    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None, pv_fp8=None):
         import torch
 
         import block_sparse_quantized_amd as bsq
@@ -90,6 +91,7 @@ class Path:
         self.bsq, self.wl, self.dev = bsq, wl, dev
         self.qk_int8 = wl.qk_int8 if qk_int8 is None else qk_int8
         self.pv_fp16 = wl.pv_fp16 if pv_fp16 is None else pv_fp16
+        self.pv_fp8 = wl.pv_fp8 if pv_fp8 is None else pv_fp8
         t0 = time.time()
         if inputs is None:
             self.q, self.k, self.v = synth.make_qkv(wl, device=dev)
@@ -118,12 +120,14 @@ class Path:
             q, k, v, out = self.qr, self.kr, self.vr, self.orr
         if wl.api == "block_sparse":
             r = bsq.block_sparse_attn(q, k, v, self.mask, filter_on=wl.filter_on,
-                                      qk_int8=self.qk_int8, pv_fp16=self.pv_fp16, stats=stats,
-                                      out=out, workspace=self.ws, prof=prof)
+                                      qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                      pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
+                                      prof=prof)
         else:
             r = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
-                                     qk_int8=self.qk_int8, pv_fp16=self.pv_fp16, stats=stats,
-                                     out=out, workspace=self.ws, prof=prof)
+                                     qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                     pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
+                                     prof=prof)
         if wl.hilbert:
             bsq.sparge_reorder(self.orr, self.perm, wl.text, self.cells, inverse=True, out=self.out)
         return r
@@ -158,15 +162,15 @@ def algorithmic_work(stats, D, qk_int8):
     return qk, pv
 
 
-def roofline(stats, D, qk_int8, attn_ms, traffic):
+def roofline(stats, D, qk_int8, attn_ms, traffic, pv_fp8=False):
     qk, pv = algorithmic_work(stats, D, qk_int8)
     t = attn_ms * 1e-3
-    if qk_int8:
-        # mixed roofline: the int8 Q K^T at the int8 peak plus the 16-bit P.V at the
-        # bf16/fp16 peak; the effective peak is the work over that minimum time
-        peak = (qk + pv) / (qk / PEAK_INT8 + pv / PEAK_BF16)
-    else:
-        peak = PEAK_BF16
+    # mixed roofline: Q K^T at the peak of its type (int8 or bf16) plus P.V at the
+    # peak of its type (fp8, or bf16/fp16); the effective peak is the work over that
+    # minimum time
+    qk_peak = PEAK_INT8 if qk_int8 else PEAK_BF16
+    pv_peak = PEAK_FP8 if pv_fp8 else PEAK_BF16
+    peak = (qk + pv) / (qk / qk_peak + pv / pv_peak)
     achieved = (qk + pv) / t
     return {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -175,16 +179,24 @@ def roofline(stats, D, qk_int8, attn_ms, traffic):
             "work_per_launch": {"qk_ops": qk, "pv_flops": pv}}
 
 
-def committed_traffic(wl_name, kernel_src):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source; else None."""
+def path_dtype(qk_int8, pv_fp16, pv_fp8):
+    """Arithmetic types of the Q.K^T and P.V products, as reported in the JSON line."""
+    pv = "fp8-pv" if pv_fp8 else ("f16-pv" if pv_fp16 else None)
+    if qk_int8:
+        return f"i8-qk/{pv or 'bf16-pv'}"
+    return f"{pv}/bf16-qk" if pv else "bf16"
+
+
+def committed_traffic(wl_name, kernel_src, dtype):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of this
+    workload and path, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"sparse_attn_{wl_name}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
+        if rec.get("kernel_source_sha256") != sha or rec.get("path", dtype) != dtype:
             return None
         return rec.get("hbm_bytes_per_launch")
     except Exception:
@@ -274,7 +286,8 @@ SWEEP_N = (8192, 16384, 32768, 65536, 131072)
 
 def sweep(wl, dev, ev, main_path, steps=3):
     """Dense-equivalent TOPS and latency over N = 8K..128K (the LLM generator, causal,
-    topk 0.5, filter on), for the int8 Q.K^T / fp16 P.V path and the bf16 path."""
+    topk 0.5, filter on), for the int8 Q.K^T path with fp16 or fp8 P.V and the bf16
+    path."""
     from block_sparse_quantized_amd import synth
     out = []
     for n in SWEEP_N:
@@ -282,14 +295,14 @@ def sweep(wl, dev, ev, main_path, steps=3):
         inputs = None
         if n == main_path.wl.N and wl.B == main_path.wl.B and wl.H == main_path.wl.H:
             inputs = (main_path.q, main_path.k, main_path.v, main_path.mask)
-        for qk8, pv16 in ((True, True), (False, False)):
-            pth = Path(wn, dev, qk_int8=qk8, pv_fp16=pv16, inputs=inputs)
+        for qk8, pv16, pv8 in ((True, True, False), (True, False, True), (False, False, False)):
+            pth = Path(wn, dev, qk_int8=qk8, pv_fp16=pv16, inputs=inputs, pv_fp8=pv8)
             inputs = (pth.q, pth.k, pth.v, pth.mask)
             _, st = pth.step(stats=True)
             s_ms, a_ms, _ = time_path(pth, ev, steps, 1)
             dense = dense_equiv_ops(wn.B, wn.H, n, wn.D, wn.causal)
-            rf = roofline(st, wn.D, qk8, a_ms, None)
-            out.append({"N": n, "path": "i8-qk/f16-pv" if qk8 else "bf16",
+            rf = roofline(st, wn.D, qk8, a_ms, None, pv8)
+            out.append({"N": n, "path": path_dtype(qk8, pv16, pv8),
                         "ms_per_step": round(s_ms, 4), "attention_ms": round(a_ms, 4),
                         "tops_dense_equiv": round(dense / (s_ms * 1e-3) / 1e12, 2),
                         "attention_frac": rf["frac"], "attention_frac_of_bf16_peak": rf["frac_of_bf16_peak"],
@@ -346,7 +359,10 @@ def main():
     dense = dense_equiv_ops(B, H, N, D, wl.causal)
     value = dense / (ms_step * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_quantized_amd", "csrc", "attn.hip")
-    roof = roofline(stats, D, path.qk_int8, ms_attn, committed_traffic(wl.name, kernel_src))
+    roof = roofline(stats, D, path.qk_int8, ms_attn,
+                    committed_traffic(wl.name, kernel_src, path_dtype(path.qk_int8, path.pv_fp16,
+                                                                      path.pv_fp8)),
+                    path.pv_fp8)
 
     extras = {}
     if not args.no_extras:
@@ -359,6 +375,16 @@ def main():
                                       "tops_dense_equiv": round(dense / (s16 * 1e-3) / 1e12, 2),
                                       "roofline": roofline(st16, D, False, a16, None)}
             del p16
+        if wl.dtype != torch.float32 and not path.pv_fp8:   # fp8 P.V takes 16-bit inputs
+            p8 = Path(wl, dev, qk_int8=True, pv_fp16=False, pv_fp8=True,
+                      inputs=(path.q, path.k, path.v, path.mask))
+            _, st8 = p8.step(stats=True)
+            s8, a8, _ = time_path(p8, ev, max(3, args.steps // 2), 1)
+            extras["i8qk_fp8pv_variant"] = {
+                "ms_per_step": round(s8, 3), "tops_dense_equiv": round(dense / (s8 * 1e-3) / 1e12, 2),
+                "roofline": roofline(st8, D, True, a8,
+                                     committed_traffic(wl.name, kernel_src, "i8-qk/fp8-pv"), True)}
+            del p8
         if wl.api != "block_sparse" and not wl.hilbert:
             pd = Path(synth.workload(wl.name, topk=1.0, filter_on=False), dev, qk_int8=False,
                       pv_fp16=False, inputs=(path.q, path.k, path.v, path.mask))
@@ -379,8 +405,7 @@ def main():
         log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
 
     density = stats["kept_blocks"] / max(1, stats["valid_blocks"])
-    dtype = ("i8-qk/f16-pv" if path.pv_fp16 else "i8-qk/bf16-pv") if path.qk_int8 else \
-        ("f16-pv/bf16-qk" if path.pv_fp16 else "bf16")
+    dtype = path_dtype(path.qk_int8, path.pv_fp16, path.pv_fp8)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -397,6 +422,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "topk": wl.topk if wl.api != "block_sparse" else None, "api": wl.api,
                    "filter_on": wl.filter_on, "qk_int8": path.qk_int8, "pv_fp16": path.pv_fp16,
+                   "pv_fp8": path.pv_fp8,
                    "hilbert": wl.hilbert},
         "roofline": roof,
         "cpu_baseline": cpu,

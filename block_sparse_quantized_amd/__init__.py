@@ -91,7 +91,7 @@ def _workspace(q: torch.Tensor, workspace: Optional[torch.Tensor]) -> Tuple[torc
 
 
 def _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask_out, stats,
-          prof=None):
+          prof=None, pv_fp8=False):
     o = SpargeOpts()
     lib().sparge_default_opts(ctypes.byref(o))
     o.scale = 0.0 if scale is None else float(scale)
@@ -100,6 +100,7 @@ def _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask
     o.filter_on = int(bool(filter_on))
     o.qk_int8 = int(bool(qk_int8))
     o.pv_fp16 = int(bool(pv_fp16))
+    o.pv_fp8 = int(bool(pv_fp8))
     o.mask_out = None if mask_out is None else ctypes.c_void_p(mask_out.data_ptr())
     st = SpargeStats() if stats else None
     o.stats = ctypes.pointer(st) if st is not None else None
@@ -123,8 +124,8 @@ def _mask_shape(q: torch.Tensor):
 def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, scale=None,
                      sim_threshold: float = 0.1, filter_lambda: float = -10.0,
                      filter_on: bool = True, qk_int8: bool = False, pv_fp16: bool = False,
-                     return_mask: bool = False, stats: bool = False, out=None, workspace=None,
-                     prof=None):
+                     pv_fp8: bool = False, return_mask: bool = False, stats: bool = False,
+                     out=None, workspace=None, prof=None):
     """Sparse attention with the on-the-fly block-mask predictor (two-stage filter).
 
     Returns ``out`` (same shape/dtype as q), plus the predicted uint8 block mask
@@ -134,7 +135,7 @@ def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, sca
         out = torch.empty_like(q)
     mask = torch.empty(_mask_shape(q), dtype=torch.uint8, device=q.device) if return_mask else None
     o, st = _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask, stats,
-                  prof)
+                  prof, pv_fp8)
     ws, nbytes = _workspace(q, workspace)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     _check(lib().sparge_topk_attn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
@@ -151,7 +152,8 @@ def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, sca
 
 def block_sparse_attn(q, k, v, mask_id=None, *, scale=None, filter_lambda: float = -10.0,
                       filter_on: bool = False, qk_int8: bool = False, pv_fp16: bool = False,
-                      stats: bool = False, out=None, workspace=None, prof=None):
+                      pv_fp8: bool = False, stats: bool = False, out=None, workspace=None,
+                      prof=None):
     """Attention under a caller-given (B, H, ceil(N/128), ceil(N/64)) 0/1 block mask."""
     if out is None:
         out = torch.empty_like(q)
@@ -161,7 +163,8 @@ def block_sparse_attn(q, k, v, mask_id=None, *, scale=None, filter_lambda: float
             raise ValueError(f"mask_id must be a {_mask_shape(q)} tensor on {q.device}")
         mask_id = mask_id.to(torch.uint8).contiguous()
         mptr = ctypes.c_void_p(mask_id.data_ptr())
-    o, st = _opts(scale, 0.1, filter_lambda, filter_on, qk_int8, pv_fp16, None, stats, prof)
+    o, st = _opts(scale, 0.1, filter_lambda, filter_on, qk_int8, pv_fp16, None, stats, prof,
+                  pv_fp8)
     ws, nbytes = _workspace(q, workspace)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     _check(lib().block_sparse_attn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mptr,

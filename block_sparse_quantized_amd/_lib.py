@@ -37,7 +37,7 @@ class SpargeOpts(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_double), ("sim_threshold", ctypes.c_double),
                 ("filter_lambda", ctypes.c_double), ("filter_on", ctypes.c_int32),
                 ("qk_int8", ctypes.c_int32), ("pv_fp16", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("mask_out", ctypes.c_void_p),
+                ("pv_fp8", ctypes.c_int32), ("mask_out", ctypes.c_void_p),
                 ("stats", ctypes.POINTER(SpargeStats)), ("prof_start", ctypes.c_void_p),
                 ("prof_attn_begin", ctypes.c_void_p), ("prof_attn_end", ctypes.c_void_p)]
 

@@ -28,7 +28,13 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
   w.kscale = take(BH * d.nK * sizeof(float));
   w.kbar = take(BH * d.nK * d.D * sizeof(float));
-  w.conv = take(3 * BH * (size_t)d.N * d.D * sizeof(uint16_t));
+  // fp32 inputs use 3 16-bit copies; fp8 P.V (16-bit inputs) its E4M3 V tiles
+  const size_t conv16 = 3 * BH * (size_t)d.N * d.D * sizeof(uint16_t);
+  const size_t vt8 = BH * (size_t)d.nK * 64 * d.D;
+  w.conv = take(conv16 > vt8 ? conv16 : vt8);
+  w.vmaxp = take(BH * d.nQ * d.D * sizeof(float));
+  w.vscale = take(BH * d.D * sizeof(float));
+  w.vinv = take(BH * d.D * sizeof(float));
   w.counters = take(8 * sizeof(unsigned long long));
   w.total = off;
   return w;
@@ -69,7 +75,7 @@ View view_of(const sparge_tensor* t) { return View{t->data, t->sB, t->sH, t->sN}
 
 sparge_status check_opts(const sparge_opts* o) {
   if (!o) return SPARGE_OK;
-  if (o->reserved != 0) return SPARGE_E_ARG;
+  if (o->pv_fp8 != 0 && o->pv_fp16 != 0) return SPARGE_E_ARG;
   if (!(o->scale >= 0.0) || isinf(o->scale)) return SPARGE_E_ARG;
   if (isnan(o->sim_threshold) || isnan(o->filter_lambda)) return SPARGE_E_ARG;
   if (o->filter_lambda > 0.0) return SPARGE_E_ARG;
@@ -182,6 +188,11 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
   p.filter_on = filter_on;
   p.qk_int8 = o.qk_int8 != 0;
   p.pv_fp16 = o.pv_fp16 != 0;
+  p.pv_fp8 = o.pv_fp8 != 0;
+  if (p.pv_fp8) {
+    p.v8t = c.at<unsigned char>(c.w.conv);
+    p.vscale = c.at<float>(c.w.vscale);
+  }
   const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
   const double log2e = 1.4426950408889634;
   p.c = (float)(scale * log2e);
@@ -223,7 +234,9 @@ sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor*
 
 // 16-bit inputs: one fused pass over Q, K and V writes the predictor's block
 // statistics, the int8 K when asked for, and the fp16 V when the P.V type differs
-// from the input's; the operands then point at the inputs or at those copies.
+// from the input's (or, for the fp8 P.V, V's per-block channel maxima, followed by
+// the scales and the E4M3 V tiles); the operands then point at the inputs or at
+// those copies.
 sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
                      const sparge_tensor* v, const sparge_opts& o, Operands& op) {
   const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
@@ -234,7 +247,8 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
   const int v_f16 = o.pv_fp16 ? 1 : op.in_f16;
   const int v_native = (v->dtype == SPARGE_F16 && v_f16) || (v->dtype == SPARGE_BF16 && !v_f16);
   uint16_t* v16 = nullptr;
-  if (v_native) {
+  float* vmaxp = o.pv_fp8 ? c.at<float>(c.w.vmaxp) : nullptr;
+  if (v_native || o.pv_fp8) {
     op.v = view_of(v);
   } else {
     v16 = c.at<uint16_t>(c.w.conv) + 2 * one;
@@ -245,7 +259,10 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
                          c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                          o.qk_int8 ? c.at<int8_t>(c.w.k8) : nullptr, chead,
                          (int64_t)c.d.nK * 64, c.at<float>(c.w.kscale), c.at<float>(c.w.kbar),
-                         v16, c.s));
+                         v16, vmaxp, c.s));
+  if (o.pv_fp8)
+    SPARGE_TRY(launch_vt8(view_of(v), v->dtype, c.d, vmaxp, c.at<float>(c.w.vscale),
+                          c.at<float>(c.w.vinv), c.at<unsigned char>(c.w.conv), c.s));
   return SPARGE_OK;
 }
 
@@ -287,6 +304,7 @@ void sparge_default_opts(sparge_opts* o) {
   o->filter_on = 1;
   o->qk_int8 = 0;
   o->pv_fp16 = 0;
+  o->pv_fp8 = 0;
 }
 
 size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t dtype,
@@ -307,6 +325,7 @@ sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
   if (!(topk > 0.0 && topk <= 1.0)) return SPARGE_E_ARG;
   sparge_opts o;
   if (opts) o = *opts; else sparge_default_opts(&o);
+  if (o.pv_fp8 && q->dtype == SPARGE_F32) return SPARGE_E_UNSUPPORTED;
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
@@ -337,14 +356,15 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
     sparge_default_opts(&o);
     o.filter_on = 0;
   }
+  if (o.pv_fp8 && q->dtype == SPARGE_F32) return SPARGE_E_UNSUPPORTED;
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   Operands op;
   bool k_ready = false;
   const int v_conv = v->dtype == SPARGE_BF16 && o.pv_fp16;
-  if (q->dtype != SPARGE_F32 && (o.qk_int8 || v_conv)) {
-    // the int8 K and the fp16 V in one pass (its block statistics go unused)
+  if (q->dtype != SPARGE_F32 && (o.qk_int8 || v_conv || o.pv_fp8)) {
+    // the int8 K and the fp16 or fp8 V in one pass (its block statistics go unused)
     if ((st = prep16(c, q, k, v, o, op)) != SPARGE_OK) return st;
     k_ready = true;
   } else if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) {
@@ -373,7 +393,7 @@ sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k
     // the statistics of the fused pass the attention path uses (no int8 K, no V)
     SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), q->dtype, c.d, c.at<double>(c.w.qmean),
                            c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
-                           nullptr, 0, 0, nullptr, nullptr, nullptr, c.s));
+                           nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, c.s));
     o.mask_out = mask_out;
     if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
     return end_stats(c, &o);
@@ -395,7 +415,8 @@ sparge_status sparge_quantize_qk(const sparge_tensor* q, const sparge_tensor* k,
     // the fused pass the attention path uses (its block statistics go unused)
     SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), k->dtype, c.d, c.at<double>(c.w.qmean),
                            c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
-                           k_codes, (int64_t)c.d.N * c.d.D, c.d.N, k_scales, k_means, nullptr, c.s));
+                           k_codes, (int64_t)c.d.N * c.d.D, c.d.N, k_scales, k_means, nullptr,
+                           nullptr, c.s));
   } else {
     SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,
                               k_scales, k_means, c.s));
@@ -443,6 +464,6 @@ const char* sparge_status_str(int32_t s) {
   }
 }
 
-int32_t sparge_abi_version(void) { return 1; }
+int32_t sparge_abi_version(void) { return 2; }
 
 }  // extern "C"

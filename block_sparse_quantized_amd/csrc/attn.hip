@@ -35,6 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_inff();
 
@@ -167,18 +168,43 @@ __device__ __forceinline__ int fv(int r) {
   if constexpr (G >= 16) return 4 * (r & 3);
   else return 4 * ((r >> 1) & 1);
 }
+// K swizzle of the fp8 P.V variant, whose sixteen lanes read rows {0..7, 32..39} +
+// a multiple of 8 (row bits 0, 1, 2 and 5 vary): those bits go to distinct bank
+// groups for 256-, 128- and 64-byte rows.
+template <int G, bool PV8>
+__device__ __forceinline__ int fkx(int r) {
+  if constexpr (!PV8) return fk<G>(r);
+  else if constexpr (G >= 16) return (r & 7) | ((r >> 2) & 8);
+  else if constexpr (G == 8) return ((r >> 1) & 3) | ((r >> 3) & 4);
+  else return ((r >> 2) & 1) | ((r >> 4) & 2);
+}
 
-template <int D, bool IN_F16, bool PV_F16, bool QK8>
+// fp8 P.V (OCP E4M3): four fp32 values rounded to nearest even into one word, the
+// first in the low byte.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float e) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, e, lo, true);
+}
+// C += A B on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E4M3 and unit
+// block scales (exponent code 127); lane (h, m) holds A[m][32h .. 32h+31] and
+// B[32h .. 32h+31][m].
+__device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int D, bool IN_F16, bool PV_F16, bool QK8, bool PV8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims d) {
   constexpr int KS16 = D / 16;                // k-steps of the 16-bit Q K^T
   constexpr int KS8 = D / 32;                 // k-steps of the int8 Q K^T
   constexpr int DT = D / 32;                  // 32-column output tiles
   constexpr int KROW = QK8 ? D : 2 * D;       // bytes per K row in LDS (no padding)
-  constexpr int VROW = 2 * D;                 // bytes per V row in LDS
+  constexpr int VROW = 2 * D;                 // bytes per V row in LDS (16-bit P.V)
   constexpr int KG = KROW / 16;               // 16-byte granules per K row
   constexpr int VG = VROW / 16;
+  // fp8 P.V stages the block's transposed E4M3 tile: D channel rows of 64 bytes
+  constexpr int VTILE = PV8 ? 64 * D : 64 * VROW;
   constexpr int KCHUNK = 64 * KROW / 1024;    // 1 KB DMA chunks per K tile
-  constexpr int VCHUNK = 64 * VROW / 1024;
+  constexpr int VCHUNK = VTILE / 1024;
   constexpr int kNU = 4 * DT;                 // (k-step, column tile) pairs of P.V
   constexpr int kVAhead = 4;                  // P.V pairs whose V reads run ahead
   constexpr int KBSTR = D + 8;                // u16 per row of the kbar hi/lo tiles
@@ -193,8 +219,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // stage never aliases reads of the other, and does not wait for it.
   __shared__ __attribute__((aligned(1024))) unsigned char Ks0[64 * KROW];
   __shared__ __attribute__((aligned(1024))) unsigned char Ks1[64 * KROW];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs0[64 * VROW];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs1[64 * VROW];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs0[VTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs1[VTILE];
   __shared__ __attribute__((aligned(16))) unsigned char Aux[AUXB];
 
   const int tid = threadIdx.x;
@@ -215,7 +241,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const unsigned short* Qp = (const unsigned short*)p.q.p + b * p.q.sB + h * p.q.sH;
   const char* Kb = QK8 ? (const char*)(p.k8 + (int64_t)bh * d.nK * 64 * D)
                        : (const char*)((const unsigned short*)p.k.p + b * p.k.sB + h * p.k.sH);
-  const char* Vb = (const char*)((const unsigned short*)p.v.p + b * p.v.sB + h * p.v.sH);
+  const char* Vb = PV8 ? (const char*)(p.v8t + (int64_t)bh * d.nK * 64 * D)
+                       : (const char*)((const unsigned short*)p.v.p + b * p.v.sB + h * p.v.sH);
   const int64_t ksrow = QK8 ? (int64_t)D : p.k.sN * 2;   // bytes between K rows in memory
   const int64_t vsrow = p.v.sN * 2;
 
@@ -302,9 +329,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     }
   }
 
+  // fp8 P.V: byte offsets of this lane's two 16-byte reads of V^T column tile 0
+  // (channel ql, keys 32hf + 16q .. +15 = logical granule 2hf + q); tile dt adds
+  // 32 rows.  Granules are swizzled by (row / 4) % 4, as the DMA stores them.
+  unsigned int v8a[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) v8a[q] = (unsigned int)(ql * 64 + 16 * ((2 * hf + q) ^ ((ql >> 2) & 3)));
+
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x16)(0.0f);
+  // fp8 P.V: the row sums come from one more MFMA with an all-ones A (E4M3 1.0 =
+  // 0x38), so they add exactly the rounded P that the P.V MFMAs see; every element
+  // of lacc then holds the lane's query-row sum over all 64 keys of each block.
+  f32x16 lacc = (f32x16)(0.0f);
   float m_true = kNegInf;   // running row max of the visited blocks (filter)
   float m_ref = kNegInf;    // reference max of the exponentials
   float m_use = 0.0f;       // m_ref, or 0 while it is -inf
@@ -324,12 +362,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 #pragma unroll
   for (int cc = 0; cc < KCW; ++cc) {
     const int r = (4 * cc + w) * (1024 / KROW) + lane / KG;
-    koff[cc] = (unsigned int)(r * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+    koff[cc] = (unsigned int)(r * ksrow + 16 * ((lane % KG) ^ fkx<KG, PV8>(r)));
   }
 #pragma unroll
   for (int cc = 0; cc < VCW; ++cc) {
-    const int r = (4 * cc + w) * (1024 / VROW) + lane / VG;
-    voff[cc] = (unsigned int)(r * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+    if constexpr (PV8) {
+      // chunk c: channel rows 16c .. 16c+15 of the contiguous E4M3 tile
+      const int r = 16 * (4 * cc + w) + lane / 4;
+      voff[cc] = (unsigned int)(r * 64 + 16 * ((lane & 3) ^ ((r >> 2) & 3)));
+    } else {
+      const int r = (4 * cc + w) * (1024 / VROW) + lane / VG;
+      voff[cc] = (unsigned int)(r * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
+    }
   }
   // Block bases as 32 x 32 -> 64-bit products (row strides are below 4 GB); one
   // wave-uniform branch per tile chooses the precomputed offsets (full block) or
@@ -349,15 +393,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         const int c = 4 * cc + w;
         const int r = c * (1024 / KROW) + lane / KG;
         const unsigned int off =
-            (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fk<KG>(r)));
+            (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fkx<KG, PV8>(r)));
         __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
       }
     }
   };
   auto dma_v = [&](int j, auto vstage) {
     unsigned char* dst = decltype(vstage)::value ? Vs1 : Vs0;
-    const char* base = Vb + (uint64_t)(unsigned int)(64 * j) * vsrow32;
-    if (64 * j + 64 <= N) {
+    // fp8 tiles are whole (tokens past N are stored as zeros)
+    const char* base = PV8 ? Vb + (uint64_t)(unsigned int)j * (64 * D)
+                           : Vb + (uint64_t)(unsigned int)(64 * j) * vsrow32;
+    if (PV8 || 64 * j + 64 <= N) {
 #pragma unroll
       for (int cc = 0; cc < VCW; ++cc)
         __builtin_amdgcn_global_load_lds((const void*)(base + voff[cc]),
@@ -374,8 +420,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     }
   };
 
-  // per-lane row of the Q.K^T A fragments: 32kt + swap23(ql), granule 2s+hf
-  const int krow_l = swap23(ql);
+  // per-lane row of the Q.K^T A fragments, granule 2s+hf: 32kt + swap23(ql), or for
+  // the fp8 P.V 16kt + krow_l with keys 32hf' .. 32hf'+31 of the P.V MFMA on the
+  // rows of lane half hf' (row m holds key 32((m/4)%2) + 16kt + 4(m/8) + m%4)
+  const int krow_l = PV8 ? (32 * ((ql >> 2) & 1) + 4 * (ql >> 3) + (ql & 3)) : swap23(ql);
+  constexpr int KTROW = PV8 ? 16 : 32;
   typedef std::conditional_t<QK8, i32x16, f32x16> acc_t;
 
   // Raw Q.K^T of the block staged in K stage KS (MFMAs only; no waits on results).
@@ -388,8 +437,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       for (int s = 0; s < KS16; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const int rr = 32 * kt + krow_l;
-          const int pg = (2 * s + hf) ^ fk<KG>(rr);
+          const int rr = KTROW * kt + krow_l;
+          const int pg = (2 * s + hf) ^ fkx<KG, PV8>(rr);
           const u16x8 kf = *(const u16x8*)(Kst + rr * KROW + 16 * pg);
           acc[kt] = mma16<IN_F16>(kf, qf[s], acc[kt]);
         }
@@ -398,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       for (int s = 0; s < KS8; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const int rr = 32 * kt + krow_l;
-          const int pg = (2 * s + hf) ^ fk<KG>(rr);
+          const int rr = KTROW * kt + krow_l;
+          const int pg = (2 * s + hf) ^ fkx<KG, PV8>(rr);
           const i32x4 kf = *(const i32x4*)(Kst + rr * KROW + 16 * pg);
           acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], acc[kt], 0, 0, 0);
         }
@@ -407,18 +456,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   };
 
   // Scores as fp32 with invisible keys at -inf, and the row max of the raw scores
-  // (both lane halves); key of sc[kt][r] is 64j + 8hf + key_off2(kt, r).
+  // (both lane halves); key of sc[kt][r] is 64j + 8hf + key_off2(kt, r), or with
+  // the fp8 P.V 64j + 32hf + 16kt + r.
   auto mask_max = [&](const acc_t (&acc)[2], int j, f32x16 (&sc)[2]) -> float {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kt][r] = (float)acc[kt][r];
     if ((64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N)) {
-      const int rel = lim - 64 * j - 8 * hf;
+      const int rel = lim - 64 * j - (PV8 ? 32 : 8) * hf;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kt][r] = key_off2(kt, r) < rel ? sc[kt][r] : kNegInf;
+        for (int r = 0; r < 16; ++r)
+          sc[kt][r] = (PV8 ? 16 * kt + r : key_off2(kt, r)) < rel ? sc[kt][r] : kNegInf;
     }
     float mraw = kNegInf;
 #pragma unroll
@@ -545,57 +596,92 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     }
     if (!skip) {
       if (__ballot(mx > m_ref + kTau) != 0ull) {
-        const float m_ref_new = fmaxf(m_ref, mx);
+        // fp8 P.V: the reference max is rounded up to an integer, so that every
+        // rescale is by a power of two and E4M3 rounds P exactly as it would round
+        // 2^(x - ceil(row max)) times that power (outside the subnormal range)
+        const float m_ref_new = PV8 ? __builtin_ceilf(fmaxf(m_ref, mx)) : fmaxf(m_ref, mx);
         const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
         const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
-        l_acc *= alpha;
+        if constexpr (PV8) lacc[0] *= alpha;   // the only element read
+        else l_acc *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         m_ref = m_ref_new;
         m_use = mu_new;
       }
-      // V^T fragments by transposing LDS reads: for k-step sg (keys 16sg..16sg+15),
-      // tile dt, lane group g = lane/16 and k = lane%16, read q in {0, 1} covers keys
-      // 16sg + 8(g/2) + 4q + k/4, columns 32dt + 16(g&1) + 4(k&3) .. +3.  The (sg, dt)
-      // pairs u = DT*sg + dt run in order with kVAhead pairs' reads in flight; the
-      // first ones are issued before the exponentials.
-      const unsigned int* va = P ? va1 : va0;
-      s16x4 fr[kVAhead + 1][2];
-      auto issue = [&](auto uc) {
-        constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
-        fr[u % (kVAhead + 1)][0] = ds_read_tr<16 * sg * VROW>(va[dt]);
-        fr[u % (kVAhead + 1)][1] = ds_read_tr<(16 * sg + 4) * VROW>(va[dt]);
-      };
-      static_for<0, kVAhead>(issue);
-      __builtin_amdgcn_sched_barrier(0);   // keep these reads ahead of the exponentials
-      // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
-      const float slope = QK8 ? slope_i8 : p.c;
-      const float offs = (QK8 ? bias : 0.0f) - m_use;
-      u32x4 pw[4];
+      if constexpr (PV8) {
+        // V^T as E4M3: tile dt's A fragment is channel 32dt + ql, keys 32hf .. +31
+        const unsigned char* Vst = P ? Vs1 : Vs0;
+        u32x4 vfr[DT][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int sg = 0; sg < 2; ++sg)
+          for (int q = 0; q < 2; ++q) vfr[dt][q] = *(const u32x4*)(Vst + v8a[q] + 2048 * dt);
+        // P = 2^(score * slope + offset - m_use) as E4M3: word q holds keys
+        // 32hf + 4q .. +3, which are sc_cur[q / 4][4(q % 4) .. +3]
+        const float slope = QK8 ? slope_i8 : p.c;
+        const float offs = (QK8 ? bias : 0.0f) - m_use;
+        i32x8 pb;
 #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const int r = 8 * sg + 2 * wd;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
-            const unsigned int pr = pack2<PV_F16>(p0, p1);
-            l_acc = add_pair<PV_F16>(pr, l_acc);
-            pw[2 * kt + sg][wd] = pr;
-          }
-      static_for<0, kNU>([&](auto uc) {
-        constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
-        if constexpr (u + kVAhead < kNU) issue(std::integral_constant<int, u + kVAhead>{});
-        constexpr int later = (kNU - 1 - u) < kVAhead ? (kNU - 1 - u) : kVAhead;
-        s16x4& f0 = fr[u % (kVAhead + 1)][0];
-        s16x4& f1 = fr[u % (kVAhead + 1)][1];
-        lds_wait<2 * later>(f0, f1);
-        const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
-      });
-    }
+        for (int q = 0; q < 8; ++q) {
+          const int kt = q >> 2, r = 4 * (q & 3);
+          float e[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + x], slope, offs));
+          pb[q] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+        }
+        const i32x8 ones = (i32x8)(0x38383838);
+        lacc = mma_fp8(ones, pb, lacc);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const i32x8 vf = __builtin_bit_cast(
+              i32x8, __builtin_shufflevector(vfr[dt][0], vfr[dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = mma_fp8(vf, pb, oacc[dt]);
+        }
+      } else {
+        // V^T fragments by transposing LDS reads: for k-step sg (keys 16sg..16sg+15),
+        // tile dt, lane group g = lane/16 and k = lane%16, read q in {0, 1} covers keys
+        // 16sg + 8(g/2) + 4q + k/4, columns 32dt + 16(g&1) + 4(k&3) .. +3.  The (sg, dt)
+        // pairs u = DT*sg + dt run in order with kVAhead pairs' reads in flight; the
+        // first ones are issued before the exponentials.
+        const unsigned int* va = P ? va1 : va0;
+        s16x4 fr[kVAhead + 1][2];
+        auto issue = [&](auto uc) {
+          constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
+          fr[u % (kVAhead + 1)][0] = ds_read_tr<16 * sg * VROW>(va[dt]);
+          fr[u % (kVAhead + 1)][1] = ds_read_tr<(16 * sg + 4) * VROW>(va[dt]);
+        };
+        static_for<0, kVAhead>(issue);
+        __builtin_amdgcn_sched_barrier(0);   // keep these reads ahead of the exponentials
+        // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
+        const float slope = QK8 ? slope_i8 : p.c;
+        const float offs = (QK8 ? bias : 0.0f) - m_use;
+        u32x4 pw[4];
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+          for (int sg = 0; sg < 2; ++sg)
+  #pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              const int r = 8 * sg + 2 * wd;
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
+              const unsigned int pr = pack2<PV_F16>(p0, p1);
+              l_acc = add_pair<PV_F16>(pr, l_acc);
+              pw[2 * kt + sg][wd] = pr;
+            }
+        static_for<0, kNU>([&](auto uc) {
+          constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
+          if constexpr (u + kVAhead < kNU) issue(std::integral_constant<int, u + kVAhead>{});
+          constexpr int later = (kNU - 1 - u) < kVAhead ? (kNU - 1 - u) : kVAhead;
+          s16x4& f0 = fr[u % (kVAhead + 1)][0];
+          s16x4& f1 = fr[u % (kVAhead + 1)][1];
+          lds_wait<2 * later>(f0, f1);
+          const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
+        });
+      }
+      }
     // the next block's scores: mask and max while the P.V MFMAs run
     if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_cur);
     j_cur = j_n1;
@@ -610,9 +696,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   }
 
   // epilogue: O = acc / l, this lane's query row, columns 32dt + 8g + 4hf + 0..3
-  const float lt = l_acc + partner32(l_acc, hf);
+  const float lt = PV8 ? lacc[0] : l_acc + partner32(l_acc, hf);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
+    // fp8 P.V: the channel scales of the E4M3 V codes, all loaded before any store
+    float4 vs[PV8 ? DT : 1][4];
+    if constexpr (PV8) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          vs[dt][g] = *(const float4*)(p.vscale + (int64_t)bh * D + 32 * dt + 8 * g + 4 * hf);
+    }
     char* ob = (char*)p.o;
     const int esz = p.out_type == kF32 ? 4 : 2;
     const int64_t rowoff = ((int64_t)b * p.osB + (int64_t)h * p.osH + (int64_t)t * p.osN) * esz;
@@ -621,8 +716,14 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * dt + 8 * g + 4 * hf;
-        const float o0 = oacc[dt][4 * g] * inv, o1 = oacc[dt][4 * g + 1] * inv;
-        const float o2 = oacc[dt][4 * g + 2] * inv, o3 = oacc[dt][4 * g + 3] * inv;
+        float o0 = oacc[dt][4 * g] * inv, o1 = oacc[dt][4 * g + 1] * inv;
+        float o2 = oacc[dt][4 * g + 2] * inv, o3 = oacc[dt][4 * g + 3] * inv;
+        if constexpr (PV8) {
+          o0 *= vs[dt][g].x;
+          o1 *= vs[dt][g].y;
+          o2 *= vs[dt][g].z;
+          o3 *= vs[dt][g].w;
+        }
         if (p.out_type == kF32) {
           *(float4*)(ob + rowoff + (int64_t)col * 4) = make_float4(o0, o1, o2, o3);
         } else if (p.out_type == kF16) {
@@ -643,12 +744,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 template <int D, bool IN_F16>
 hipError_t launch_d(const AttnParams& p, const Dims& d, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
-  if (p.qk_int8) {
-    if (p.pv_fp16) sparse_attn_kernel<D, IN_F16, true, true><<<grid, 256, 0, s>>>(p, d);
-    else sparse_attn_kernel<D, IN_F16, IN_F16, true><<<grid, 256, 0, s>>>(p, d);
+  if (p.pv_fp8) {
+    if (p.qk_int8) sparse_attn_kernel<D, IN_F16, false, true, true><<<grid, 256, 0, s>>>(p, d);
+    else sparse_attn_kernel<D, IN_F16, false, false, true><<<grid, 256, 0, s>>>(p, d);
+  } else if (p.qk_int8) {
+    if (p.pv_fp16) sparse_attn_kernel<D, IN_F16, true, true, false><<<grid, 256, 0, s>>>(p, d);
+    else sparse_attn_kernel<D, IN_F16, IN_F16, true, false><<<grid, 256, 0, s>>>(p, d);
   } else {
-    if (p.pv_fp16) sparse_attn_kernel<D, IN_F16, true, false><<<grid, 256, 0, s>>>(p, d);
-    else sparse_attn_kernel<D, IN_F16, IN_F16, false><<<grid, 256, 0, s>>>(p, d);
+    if (p.pv_fp16) sparse_attn_kernel<D, IN_F16, true, false, false><<<grid, 256, 0, s>>>(p, d);
+    else sparse_attn_kernel<D, IN_F16, IN_F16, false, false><<<grid, 256, 0, s>>>(p, d);
   }
   return hipGetLastError();
 }

@@ -10,7 +10,10 @@
 //     "Key features"; [readme] "Avalible API"): kbar_j = fp32(fp64 row sum / rows),
 //     k'' = fp32(k) - kbar_j, a = max|k''| over the block, codes =
 //     clamp(rint(k'' * (127 / a)), -127, 127), step a / 127, all in IEEE fp32;
-//   * optionally V rounded (to nearest even) from bf16 to fp16 for the fp16 P.V.
+//   * optionally V rounded (to nearest even) from bf16 to fp16 for the fp16 P.V, or,
+//     for the fp8 P.V, the block's per-channel max |v| (reduced over the sequence by
+//     vscale_kernel; vt8_kernel then writes V as E4M3 codes in transposed 64-token
+//     tiles, see below).
 //
 // One workgroup of 256 threads per (b, h, Q block i): Q rows 128i..128i+127, the
 // K blocks 2i and 2i+1 over the same rows, and the same V rows.  Every 16-byte
@@ -46,12 +49,15 @@ __device__ __forceinline__ signed char quant_code(float x, float inv) {
   return (signed char)(int)c;
 }
 
-template <int DT, int D, bool QUANT, bool VCONV>
+// VMODE: 0 leave V alone, 1 write the fp16 copy, 2 write per-channel max |v| of
+// the block's rows (fp8 P.V).
+template <int DT, int D, bool QUANT, int VMODE>
 __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims d, double* qmean,
                                                    double* qsim, double* kmean, double* ksim,
                                                    int8_t* codes, int64_t codes_head_stride,
                                                    int64_t codes_rows, float* kscale, float* kbar,
-                                                   uint16_t* v16) {
+                                                   uint16_t* v16, float* vmaxp) {
+  constexpr bool VCONV = VMODE != 0;
   constexpr bool F16 = DT == kF16;
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int NCH = 128 * CH / 256;     // chunks per thread
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
   __shared__ double sq_s[4];
   __shared__ float mean_s[2][D];
   __shared__ float amax_s[4][2];
+  __shared__ float vmx_s[VMODE == 2 ? 256 / (D / 8) : 1][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x / d.nQ, i = blockIdx.x - bh * d.nQ;
@@ -86,8 +93,35 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
     if constexpr (VCONV) vr[kk] = ok ? *(const uint4*)(vb + rr * v.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
   }
 
+  // V, fp8 P.V: per-channel max |v| over the block's rows (each thread's chunk is 8
+  // channels of one row; rows past N were loaded as zeros)
+  if constexpr (VMODE == 2) {
+    float mx[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mx[c] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NCH; ++kk) {
+      const unsigned int wd[4] = {vr[kk].x, vr[kk].y, vr[kk].z, vr[kk].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mx[2 * c] = fmaxf(mx[2 * c], fabsf(u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16)));
+        mx[2 * c + 1] = fmaxf(mx[2 * c + 1], fabsf(u16_to_f32((unsigned short)(wd[c] >> 16), F16)));
+      }
+    }
+    // thread t covers channels 8 (t % CH) .. +7 of rows t / CH + (256 / CH) kk
+    const int ch = tid % CH, rg = tid / CH;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vmx_s[rg][8 * ch + c] = mx[c];
+    __syncthreads();
+    if (tid < D) {
+      float m = 0.0f;
+      for (int r = 0; r < 256 / CH; ++r) m = fmaxf(m, vmx_s[r][tid]);
+      vmaxp[((int64_t)bh * d.nQ + i) * D + tid] = m;
+    }
+  }
+
   // V: fp16 copy, rows < N only
-  if constexpr (VCONV) {
+  if constexpr (VMODE == 1) {
 #pragma unroll
     for (int kk = 0; kk < NCH; ++kk) {
       const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
@@ -283,26 +317,100 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
   }
 }
 
+// fp8 P.V, per (b, h): the channel maxima over all Q blocks, then the E4M3
+// scale s_d = fp32(max / 448) and its inverse fp32(448 / max) (0 for an all-zero
+// channel).
+__global__ __launch_bounds__(128) void vscale_kernel(const float* vmaxp, Dims d, float* vscale,
+                                                     float* vinv) {
+  const int bh = blockIdx.x;
+  for (int c = threadIdx.x; c < d.D; c += 128) {
+    float m = 0.0f;
+    for (int i = 0; i < d.nQ; ++i) m = fmaxf(m, vmaxp[((int64_t)bh * d.nQ + i) * d.D + c]);
+    vscale[(int64_t)bh * d.D + c] = m / 448.0f;
+    vinv[(int64_t)bh * d.D + c] = m > 0.0f ? 448.0f / m : 0.0f;
+  }
+}
+
+// fp8 P.V: V as E4M3 codes e4m3(fp32(v * inv_d)) (round to nearest even) in
+// transposed 64-token tiles, vt[((bh * nK + j) * D + c) * 64 + r] = channel c of
+// token 64j + r, tokens past N zero: the attention kernel stages one tile as one
+// contiguous D * 64-byte read.  One workgroup per (b, h, 64-token block); the
+// block's codes are transposed through LDS.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void vt8_kernel(View v, Dims d, const float* vinv, unsigned char* vt) {
+  constexpr bool F16 = DT == kF16;
+  constexpr int TP = 64 + 4;   // LDS bytes per channel row (4-byte aligned, staggered banks)
+  __shared__ __attribute__((aligned(16))) unsigned char t[D * TP];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / d.nK, j = blockIdx.x - bh * d.nK;
+  const int b = bh / d.H, h = bh - b * d.H;
+  const unsigned short* vb = (const unsigned short*)v.p + (int64_t)b * v.sB + (int64_t)h * v.sH;
+  const float* iv = vinv + (int64_t)bh * D;
+  // 64 rows x D channels: each thread converts 8 channels of one row per pass
+  constexpr int CH = D / 8;
+  for (int e = tid; e < 64 * CH; e += 256) {
+    const int r = e / CH, ch = e % CH;
+    const int n = 64 * j + r;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < d.N) w = *(const uint4*)(vb + (int64_t)n * v.sN + 8 * ch);
+    const unsigned int wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int c0 = 8 * ch + 2 * c;
+      const float x0 = u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16) * iv[c0];
+      const float x1 = u16_to_f32((unsigned short)(wd[c] >> 16), F16) * iv[c0 + 1];
+      const unsigned int pk = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+      t[c0 * TP + r] = (unsigned char)(pk & 0xffu);
+      t[(c0 + 1) * TP + r] = (unsigned char)((pk >> 8) & 0xffu);
+    }
+  }
+  __syncthreads();
+  // the tile as D rows of 64 bytes, 16 bytes per thread
+  unsigned char* dst = vt + ((int64_t)bh * d.nK + j) * (64 * D);
+  for (int e = tid; e < D * 4; e += 256) {
+    const int c = e >> 2, g = e & 3;
+    const unsigned int* src = (const unsigned int*)(t + c * TP + 16 * g);
+    *(uint4*)(dst + 16 * e) = make_uint4(src[0], src[1], src[2], src[3]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_vt8(const View& v, int dtype, const Dims& d, const float* vmaxp, float* vscale,
+                      float* vinv, unsigned char* vt, hipStream_t s) {
+  vscale_kernel<<<dim3((unsigned)(d.B * d.H)), 128, 0, s>>>(vmaxp, d, vscale, vinv);
+  const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nK));
+  if (dtype == kF16) {
+    if (d.D == 64) vt8_kernel<kF16, 64><<<grid, 256, 0, s>>>(v, d, vinv, vt);
+    else vt8_kernel<kF16, 128><<<grid, 256, 0, s>>>(v, d, vinv, vt);
+  } else {
+    if (d.D == 64) vt8_kernel<kBF16, 64><<<grid, 256, 0, s>>>(v, d, vinv, vt);
+    else vt8_kernel<kBF16, 128><<<grid, 256, 0, s>>>(v, d, vinv, vt);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
                        double* qmean, double* qsim, double* kmean, double* ksim, int8_t* codes,
                        int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
-                       uint16_t* v16, hipStream_t s) {
+                       uint16_t* v16, float* vmaxp, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
-  const bool quant = codes != nullptr, vconv = v16 != nullptr;
+  const bool quant = codes != nullptr;
+  const int vmode = v16 != nullptr ? 1 : (vmaxp != nullptr ? 2 : 0);
 #define SPARGE_PREP(DTV, DV, QV, VV)                                                             \
   prep_kernel<DTV, DV, QV, VV><<<grid, 256, 0, s>>>(q, k, v, d, qmean, qsim, kmean, ksim, codes, \
-                                                    codes_head_stride, codes_rows, kscale, kbar, v16)
+                                                    codes_head_stride, codes_rows, kscale, kbar, v16, \
+                                                    vmaxp)
+#define SPARGE_PREP_Q(DTV, DV, QV)                                 \
+  do {                                                             \
+    if (vmode == 1) SPARGE_PREP(DTV, DV, QV, 1);                   \
+    else if (vmode == 2) SPARGE_PREP(DTV, DV, QV, 2);              \
+    else SPARGE_PREP(DTV, DV, QV, 0);                              \
+  } while (0)
 #define SPARGE_PREP_D(DTV, DV)                                     \
   do {                                                             \
-    if (quant) {                                                   \
-      if (vconv) SPARGE_PREP(DTV, DV, true, true);                 \
-      else SPARGE_PREP(DTV, DV, true, false);                      \
-    } else {                                                       \
-      if (vconv) SPARGE_PREP(DTV, DV, false, true);                \
-      else SPARGE_PREP(DTV, DV, false, false);                     \
-    }                                                              \
+    if (quant) SPARGE_PREP_Q(DTV, DV, true);                       \
+    else SPARGE_PREP_Q(DTV, DV, false);                            \
   } while (0)
   if (dtype == kF16) {
     if (d.D == 64) SPARGE_PREP_D(kF16, 64);
@@ -312,6 +420,7 @@ hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, c
     else SPARGE_PREP_D(kBF16, 128);
   }
 #undef SPARGE_PREP_D
+#undef SPARGE_PREP_Q
 #undef SPARGE_PREP
   return hipGetLastError();
 }

@@ -44,7 +44,10 @@ struct Workspace {
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
   size_t lists, counts;            // uint16 kept-block lists (BH, nQ, lstride), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
-  size_t conv;                     // 16-bit copies of q, k (fp32 inputs) and v (3 x BH*N*D)
+  size_t conv;                     // 16-bit copies of q, k (fp32 inputs) and v (3 x BH*N*D);
+                                   // with fp8 P.V (16-bit inputs only) the E4M3 V tiles
+  size_t vmaxp, vscale, vinv;      // fp8 P.V: per-block channel max |v| (BH, nQ, D), fp32
+                                   // channel scales and inverses (BH, D)
   size_t counters;                 // 8 x uint64 stats counters
   size_t total;
 };
@@ -89,11 +92,18 @@ hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes
 // self-similarities of launch_block_stats, plus, when codes != nullptr, the
 // block-smoothed int8 K of launch_quant_k (codes with D bytes per row, rows below
 // codes_rows written, those past N as zeros), and, when v16 != nullptr, V rounded
-// to fp16 into a contiguous (B, H, N, D) buffer.
+// to fp16 into a contiguous (B, H, N, D) buffer, or, when vmaxp != nullptr, the
+// per-block channel maxima of |v| (B, H, nQ, D) for the fp8 P.V.
 hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, const Dims& d,
                        double* qmean, double* qsim, double* kmean, double* ksim, int8_t* codes,
                        int64_t codes_head_stride, int64_t codes_rows, float* kscale, float* kbar,
-                       uint16_t* v16, hipStream_t s);
+                       uint16_t* v16, float* vmaxp, hipStream_t s);
+
+// fp8 P.V: per-channel scales from the per-block maxima of launch_prep (vmaxp), then
+// V as E4M3 codes in transposed 64-token tiles: vt[((bh * nK + j) * D + c) * 64 + r]
+// is channel c of token 64j + r (zero for tokens past N).
+hipError_t launch_vt8(const View& v, int dtype, const Dims& d, const float* vmaxp, float* vscale,
+                      float* vinv, unsigned char* vt, hipStream_t s);
 
 // int8 Q codes with one step per 32 rows (the kernel the attention kernel mirrors).
 hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
@@ -106,7 +116,7 @@ struct AttnParams {
   int64_t osB, osH, osN;
   int in_f16;            // q/k/v element type: 1 = fp16, 0 = bf16
   int out_type;          // ElemType of the output
-  int causal, filter_on, qk_int8, pv_fp16;
+  int causal, filter_on, qk_int8, pv_fp16, pv_fp8;
   float c;               // scale * log2(e)
   float lam2;            // filter lambda * log2(e)
   const uint16_t* lists;
@@ -114,6 +124,8 @@ struct AttnParams {
   const int8_t* k8;      // int8 path: codes, (BH, nK*64, D)
   const float* kscale;   // (BH, nK)
   const float* kbar;     // (BH, nK, D)
+  const unsigned char* v8t;  // fp8 P.V: E4M3 V tiles (BH, nK, D, 64)
+  const float* vscale;       // fp8 P.V: channel scales (BH, D)
   unsigned long long* counters;  // nullable: [2] = group updates, [3] = skipped updates
 };
 

@@ -51,6 +51,7 @@ class Workload:
     filter_on: bool = True
     qk_int8: bool = False
     pv_fp16: bool = False
+    pv_fp8: bool = False
     api: str = "topk"              # "topk" or "block_sparse"
     text: int = 0                  # text-token prefix length (visual workloads)
     grid: Tuple[int, ...] = ()     # visual grid shape after the prefix

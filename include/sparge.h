@@ -86,7 +86,15 @@ typedef struct {
                             an exact q.kbar term.  Default 0 (16-bit Q K^T). */
   int32_t pv_fp16;       /* 1: P and V rounded to fp16 for P.V; 0: the input's
                             16-bit type (bfloat16 for fp32 inputs).  Default 0. */
-  int32_t reserved;      /* must be 0 */
+  int32_t pv_fp8;        /* 1: P.V in OCP FP8 E4M3 (the 8-bit-float P.V of the
+                            SageAttention2 base, [readme] "Installation" fp8
+                            requirements; [topgit] "Key features"): V one fp32
+                            scale per (b, h, channel) over the sequence, codes
+                            e4m3(v * 448 / max|v|); each softmax numerator rounded
+                            to E4M3 and the row normaliser summed over the
+                            rounded numerators; fp32 accumulation.  16-bit inputs
+                            only (SPARGE_E_UNSUPPORTED for fp32); may not be
+                            combined with pv_fp16 (SPARGE_E_ARG).  Default 0. */
   uint8_t* mask_out;     /* optional device (B, H, ceil(N/128), ceil(N/64)) uint8:
                             receives the predicted 0/1 block mask */
   sparge_stats* stats;   /* optional HOST pointer; when set the call waits for the

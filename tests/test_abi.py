@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     missing = [n for n in names if n not in exported]
     assert not missing, f"declared but not exported: {missing}"
     assert set(names) == set(L.PROTOTYPES), "binding prototypes must cover exactly the header"
-    assert lib.sparge_abi_version() == 1
+    assert lib.sparge_abi_version() == 2
 
 
 def test_struct_layout_matches_c_compiler():
@@ -103,6 +103,15 @@ def test_validation_errors_topk(lib):
     bad.filter_lambda = -10.0
     bad.scale = -1.0
     assert call_topk(lib, q, k, v, o, opts=ctypes.byref(bad)) == -4
+    bad.scale = 0.0
+    bad.pv_fp8, bad.pv_fp16 = 1, 1                                         # two P.V types
+    assert call_topk(lib, q, k, v, o, opts=ctypes.byref(bad)) == -4
+    bad.pv_fp16 = 0                                                         # fp8 P.V, fp32 inputs
+    f32 = [T(dtype=L.SPARGE_F32, data=FAKE + 16384 * i) for i in range(4)]
+    assert call_topk(lib, *f32, opts=ctypes.byref(bad)) == -5
+    r = lib.block_sparse_attn(*(ctypes.byref(t) for t in f32[:3]), None, ctypes.byref(f32[3]),
+                              ctypes.byref(bad), FAKE, 1 << 40, None)
+    assert r == -5
 
 
 def test_validation_errors_other_entry_points(lib):
@@ -139,7 +148,7 @@ def test_default_opts(lib):
     o = L.SpargeOpts()
     lib.sparge_default_opts(ctypes.byref(o))
     assert (o.scale, o.sim_threshold, o.filter_lambda) == (0.0, 0.1, -10.0)
-    assert (o.filter_on, o.qk_int8, o.pv_fp16, o.reserved) == (1, 0, 0, 0)
+    assert (o.filter_on, o.qk_int8, o.pv_fp16, o.pv_fp8) == (1, 0, 0, 0)
     assert not o.mask_out and not o.stats
 
 

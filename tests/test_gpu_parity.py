@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 TOL16 = 2e-2
 TOL8 = 5e-2
+TOLF8 = 2e-2     # fp8 P.V against the oracle's fp8 P.V simulation on the same logits
 
 
 def say(*a):
@@ -82,6 +83,21 @@ def unexcused_mismatches(gpu_mask, ora_mask, infos, theta=0.1):
             else:
                 bad += 1
     return bad, excused
+
+
+def oracle_mask_and_rows(q, k, gm, topk, causal):
+    """The oracle's own block mask (the GPU mask must match it up to excused near-ties)
+    and a (B, H, N) flag of the query rows whose block row is identical on both sides:
+    outputs are compared on those rows, with the oracle's mask as its input."""
+    om, infos = oracle_predict(q, k, so.OracleParams(topk=topk, causal=causal))
+    g = gm.cpu().numpy().astype(bool)
+    bad, exc = unexcused_mismatches(g, om, infos)
+    assert bad == 0
+    same = (g == om).all(axis=3)                                   # (B, H, nQ)
+    N = q.shape[2]
+    rows = np.repeat(same, so.BQ, axis=2)[:, :, :N]
+    assert rows.mean() > 0.9
+    return om, rows
 
 
 def oracle_outputs(q, k, v, mask, causal, lam=None, scale=None):
@@ -188,7 +204,7 @@ def test_tiny_workload_end_to_end(dev):
     om, infos = oracle_predict(q, k, so.OracleParams(topk=wl.topk, causal=wl.causal))
     bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
     assert bad == 0 and exc == 0
-    ref, _ = oracle_outputs(q, k, v, gm.cpu().numpy().astype(bool), wl.causal)
+    ref, _ = oracle_outputs(q, k, v, om, wl.causal)
     err = np.abs(f64(out) - ref).max()
     say(f"tiny workload err {err:.3e}, density {gm.float().mean().item():.3f}")
     assert err < TOL16
@@ -256,19 +272,107 @@ def test_int8_attention(dev, N, D, causal, pv16):
     q, k, v = synth.make_qkv(wl, device=dev)
     out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, causal, qk_int8=True, pv_fp16=pv16,
                                    filter_on=False, return_mask=True)
-    mask = gm.cpu().numpy().astype(bool)
+    mask, rows = oracle_mask_and_rows(q, k, gm, 0.5, causal)
     ref, _ = oracle_outputs(q, k, v, mask, causal)
-    err = np.abs(f64(out) - ref).max()
+    err = np.abs(f64(out) - ref)[rows].max()
     qn, kn, vn = f64(q), f64(k), f64(v)
     sim_err = 0.0
     for h in range(2):
         o8 = so.attend_head_int8_sim(qn[0, h].astype(np.float32), kn[0, h].astype(np.float32),
                                      vn[0, h], mask[0, h], causal,
                                      pv_round="fp16" if pv16 else "bf16")
-        sim_err = max(sim_err, np.abs(f64(out)[0, h] - o8).max())
+        sim_err = max(sim_err, np.abs(f64(out)[0, h] - o8)[rows[0, h]].max())
     say(f"int8 N={N} D={D}: err vs fp64 {err:.3e}, vs int8 simulation {sim_err:.3e}")
     assert err < TOL8
     assert sim_err < TOL16
+
+
+# ------------------------------------------------------------------ fp8 P.V
+
+def pv8_oracle(q, k, v, mask, causal, lam, qk):
+    qn, kn, vn = f64(q), f64(k), f64(v)
+    B, H = qn.shape[:2]
+    out = np.zeros_like(qn)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = so.attend_head_pv8_sim(qn[b, h], kn[b, h], vn[b, h], mask[b, h], causal,
+                                               lam=lam, qk=qk)
+    return out
+
+
+@pytest.mark.parametrize("N,D,dtype,qk8,filt", [
+    (1000, 128, torch.bfloat16, False, False), (700, 64, torch.float16, True, True),
+    (129, 128, torch.bfloat16, True, False), (64, 64, torch.bfloat16, False, True),
+    (513, 128, torch.float16, False, True), (1, 128, torch.bfloat16, True, False)])
+def test_fp8_pv_block_sparse_matches_oracle(dev, N, D, dtype, qk8, filt):
+    say(f"fp8 P.V block_sparse N={N} D={D} {dtype} qk_int8={qk8} filter={filt}")
+    B, H = 2, 2
+    q, k, v = rand_qkv(B, H, N, D, dtype, dev, seed=N + D + 7)
+    nQ, nK = so.num_blocks(N)
+    g = torch.Generator().manual_seed(8)
+    mask = (torch.rand((B, H, nQ, nK), generator=g) < 0.45).to(torch.uint8)
+    mask[0, 0, 0] = 0                       # an empty block row -> zero output
+    mask[1, 1, :, -1] = 1                   # ragged last K block kept
+    out = bsq.block_sparse_attn(q, k, v, mask.to(dev), pv_fp8=True, qk_int8=qk8, filter_on=filt)
+    torch.cuda.synchronize()
+    mnp = mask.numpy().astype(bool)
+    ref = pv8_oracle(q, k, v, mnp, False, -10.0 if filt else None, "int8" if qk8 else "exact")
+    exact, _ = oracle_outputs(q, k, v, mnp, False, lam=-10.0 if filt else None)
+    err = np.abs(f64(out) - ref).max()
+    say(f"  max abs err vs fp8 simulation {err:.3e}, vs fp64 {np.abs(f64(out) - exact).max():.3e}")
+    assert err < TOLF8
+    assert np.all(f64(out)[0, 0, :min(N, 128)] == 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_fp8_pv_exact_when_p_and_v_are_representable(dev, dtype):
+    # logits n ln 2 (integers n in [-6, 2]) and V on the E4M3 grid times 1/8 with
+    # every channel's max |v| = 56: every P and V code is exact, so the fp8 path
+    # equals dense attention up to fp32 accumulation
+    B, H, N, D = 1, 2, 1000, 128
+    r = np.random.default_rng(21)
+    q = np.zeros((B, H, N, D))
+    q[..., 0] = 1.0
+    k = np.zeros((B, H, N, D))
+    k[..., 0] = r.integers(-6, 3, size=(B, H, N))
+    e = np.array([(1 + m / 8) * 2.0 ** (x - 7) for x in range(1, 16) for m in range(8)
+                  if not (x == 15 and m == 7)])
+    v = r.choice(e, size=(B, H, N, D)) * r.choice([-1.0, 1.0], size=(B, H, N, D)) * 0.125
+    v[:, :, 5, :] = 56.0
+    qt, kt, vt = (torch.from_numpy(x).to(dtype).to(dev) for x in (q, k, v))
+    out = bsq.block_sparse_attn(qt, kt, vt, None, scale=math.log(2.0), pv_fp8=True)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)),
+                                         scale=math.log(2.0)).numpy()
+    got = f64(out)
+    err = np.abs(got - ref).max()
+    say(f"fp8 P.V exact case {dtype}: err {err:.3e}")
+    # only the output's rounding to the input type (half an ulp) and fp32 sums remain
+    rel = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-4)
+
+
+@pytest.mark.parametrize("N,D,causal,qk8", [(2000, 128, True, True), (1500, 64, False, False),
+                                            (300, 128, True, False)])
+def test_fp8_pv_topk(dev, N, D, causal, qk8):
+    wl = synth.workload("llm8k", H=2, N=N, D=D)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, causal, qk_int8=qk8, pv_fp8=True,
+                                   filter_on=True, return_mask=True)
+    mask, rows = oracle_mask_and_rows(q, k, gm, 0.5, causal)
+    ref = pv8_oracle(q, k, v, mask, causal, -10.0, "int8" if qk8 else "exact")
+    err = np.abs(f64(out) - ref)[rows].max()
+    vmax = np.abs(f64(v)).max()
+    say(f"fp8 P.V topk N={N} D={D} causal={causal} int8={qk8}: err {err:.3e} (max|v| {vmax:.2f})")
+    assert err < TOLF8 * max(1.0, vmax / 4)
+
+
+def test_fp8_pv_fp32_inputs_unsupported(dev):
+    q, k, v = rand_qkv(1, 1, 256, 64, torch.float32, dev, seed=1)
+    with pytest.raises(Exception):
+        bsq.sparge_topk_attn(q, k, v, 0.5, False, pv_fp8=True)
+    with pytest.raises(Exception):
+        bsq.sparge_topk_attn(*rand_qkv(1, 1, 256, 64, torch.bfloat16, dev, seed=1), 0.5, False,
+                             pv_fp8=True, pv_fp16=True)
 
 
 # -------------------------------------------------------------- Hilbert reorder
@@ -316,19 +420,25 @@ def run_workload(wl, q, k, v, mask=None, stats=False):
     """The exact call sequence bench.py times for a workload."""
     if wl.api == "block_sparse":
         return bsq.block_sparse_attn(q, k, v, mask, filter_on=wl.filter_on, qk_int8=wl.qk_int8,
-                                     pv_fp16=wl.pv_fp16, stats=stats)
+                                     pv_fp16=wl.pv_fp16, pv_fp8=wl.pv_fp8, stats=stats)
     return bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
-                                qk_int8=wl.qk_int8, pv_fp16=wl.pv_fp16, return_mask=True,
-                                stats=stats)
+                                qk_int8=wl.qk_int8, pv_fp16=wl.pv_fp16, pv_fp8=wl.pv_fp8,
+                                return_mask=True, stats=stats)
 
 
-def sample_groups(B, H, N, n, seed, causal):
+def sample_groups(B, H, N, n, seed, causal, ok=None):
+    """n (b, h, block row, 32-row group) picks, the ragged last group first; with
+    ok (B, H, nQ) only block rows where ok holds."""
     r = np.random.default_rng(seed)
     nQ = (N + 127) // 128
-    picks = [(0, 0, nQ - 1, (N - 1 - 128 * (nQ - 1)) // 32)]   # the ragged last group
+    picks = []
+    if ok is None or ok[0, 0, nQ - 1]:
+        picks.append((0, 0, nQ - 1, (N - 1 - 128 * (nQ - 1)) // 32))   # the ragged last group
     while len(picks) < n:
         b, h = int(r.integers(B)), int(r.integers(H))
         i = int(r.integers(nQ)) if not causal or r.random() < 0.5 else nQ - 1 - int(r.integers(4))
+        if ok is not None and not ok[b, h, i]:
+            continue
         gmax = (min(N, 128 * i + 128) - 128 * i + 31) // 32
         picks.append((b, h, i, int(r.integers(gmax))))
     return picks
@@ -344,7 +454,12 @@ def test_full_workload(dev, name):
     if wl.hilbert:
         cells = int(np.prod(wl.grid))
         perm = bsq.sparge_hilbert_perm3d(*wl.grid).to(dev)
+        full = np.concatenate([np.arange(wl.text), wl.text + hilbert_cell_order(*wl.grid)])
+        fidx = torch.from_numpy(full).to(dev)
+        want = [t[:, :, fidx] for t in (q, k, v)]          # the oracle's order, by indexing
         q, k, v = (bsq.sparge_reorder(t, perm, wl.text, cells) for t in (q, k, v))
+        assert all(torch.equal(a, b) for a, b in zip((q, k, v), want))
+        q, k, v = want
     res = run_workload(wl, q, k, v, mask_in, stats=True)
     torch.cuda.synchronize()
     if wl.api == "block_sparse":
@@ -352,18 +467,22 @@ def test_full_workload(dev, name):
         mask = mask_in.cpu().numpy().astype(bool)
     else:
         out, gm, st = res
-        mask = gm.cpu().numpy().astype(bool)
         om, infos = oracle_predict(q, k, so.OracleParams(topk=wl.topk, causal=wl.causal))
         bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
-        say(f"  mask: unexcused {bad}, excused {exc}, density {mask.mean():.3f}")
+        say(f"  mask: unexcused {bad}, excused {exc}, density {om.mean():.3f}")
         assert bad == 0
+        assert st["kept_blocks"] == int(gm.cpu().numpy().astype(bool).sum())
+        same = (gm.cpu().numpy().astype(bool) == om).all(axis=3)
+        mask = om
     say(f"  stats {st}")
-    assert st["kept_blocks"] == int(mask.sum())
+    if wl.api == "block_sparse":
+        assert st["kept_blocks"] == int(mask.sum())
+        same = np.ones(mask.shape[:3], dtype=bool)
     lam = -10.0 if wl.filter_on else None
     tol = TOL8 if wl.qk_int8 else TOL16
     B, H, N, D = q.shape
     worst = 0.0
-    for (b, h, i, g) in sample_groups(B, H, N, 8, seed=len(name), causal=wl.causal):
+    for (b, h, i, g) in sample_groups(B, H, N, 8, seed=len(name), causal=wl.causal, ok=same):
         qn, kn, vn = f64(q[b, h]), f64(k[b, h]), f64(v[b, h])
         ref = so.attend_rows(qn, kn, vn, mask[b, h], [(i, g)], wl.causal, lam=lam)[(i, g)]
         t0 = 128 * i + 32 * g
