@@ -44,6 +44,7 @@ class OracleParams:
     """Knobs of the method.  Defaults are the readings where the pages are silent."""
 
     topk: float = 0.5            # fraction of candidate blocks kept per block row
+    cdf: Optional[float] = None  # when set: keep by softmax mass instead (cdf_keep_count)
     causal: bool = False
     theta: float = 0.1           # self-similarity threshold (reading; not on the pages)
     lam: Optional[float] = None  # filter threshold in natural-log logit units; None = off
@@ -125,6 +126,28 @@ def keep_count(C: int, topk: float) -> int:
     return int(min(C, max(1, math.ceil(topk * C - 1e-9))))
 
 
+def cdf_keep_count(scores_row: np.ndarray, cand: np.ndarray, tau: float) -> int:
+    """How many candidates a row keeps under the threshold (non-top-k) selection.
+
+    The pages name threshold-driven variants of the predictor next to the top-k one
+    ([readme] "Avalible API" and [gittools] API list: the ``meansim`` calls without
+    ``topk``) and advise calibrating the thresholds per layer and head ([chapterpal]
+    recommendations), but give no formula.  Reading: rank the candidates as
+    ``select_row`` does (score descending, block index ascending), take the row
+    softmax p of the compressed map over the candidates (fp64), and keep the
+    shortest prefix of the ranking whose cumulative p, summed in ranking order,
+    reaches tau: k = 1 + #{m : p_(0) + ... + p_(m) < tau}, at most C.
+    """
+    js = np.flatnonzero(cand)
+    if js.size == 0:
+        return 0
+    s = scores_row[js]
+    order = np.lexsort((js, -s))
+    e = np.exp(s[order] - s.max())
+    cum = np.cumsum(e / e.sum())
+    return int(min(js.size, 1 + int((cum < tau).sum())))
+
+
 def select_row(scores: np.ndarray, cand: np.ndarray, k: int) -> np.ndarray:
     """The k best candidates by (score descending, block index ascending).
 
@@ -143,7 +166,8 @@ def predict_mask(q: np.ndarray, k: np.ndarray, p: OracleParams) -> Tuple[np.ndar
 
     M[i, j] = valid(i, j) and (Q block i not similar, or K block j not similar, or
     j among the top-k candidates of row i), candidates being the valid, similar K
-    blocks of the row.  Q and K enter raw (no smoothing) for every precision option.
+    blocks of the row; with ``p.cdf`` set, k comes from ``cdf_keep_count``.  Q and K
+    enter raw (no smoothing) for every precision option.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -164,7 +188,7 @@ def predict_mask(q: np.ndarray, k: np.ndarray, p: OracleParams) -> Tuple[np.ndar
     for i in range(nQ):
         cand = valid[i] & simk
         C = int(cand.sum())
-        kk = keep_count(C, p.topk)
+        kk = keep_count(C, p.topk) if p.cdf is None else cdf_keep_count(S[i], cand, p.cdf)
         sel = select_row(S[i], cand, kk)
         row = valid[i] & (~simq[i] | ~simk)
         row[sel] = True

@@ -233,6 +233,79 @@ def test_topk_on_softmax_equals_topk_on_logits():
         assert abs(p[cand].sum() - 1) < 1e-12
 
 
+def test_cdf_keep_count_brute_force():
+    # the kept count is the smallest size of ANY candidate subset whose softmax mass
+    # reaches tau (the best blocks reach it first), found by enumeration
+    r = np.random.default_rng(41)
+    for trial in range(300):
+        n = int(r.integers(1, 10))
+        s = r.standard_normal(n) * 2
+        cand = r.random(n) < 0.8
+        if not cand.any():
+            assert so.cdf_keep_count(s, cand, 0.5) == 0
+            continue
+        tau = float(r.uniform(0.05, 1.0))
+        js = np.flatnonzero(cand)
+        w = np.exp(s[js] - s[js].max())
+        w /= w.sum()
+        best = None
+        for kk in range(1, js.size + 1):
+            if max(sum(c) for c in itertools.combinations(w, kk)) >= tau - 1e-12:
+                best = kk
+                break
+        best = js.size if best is None else best
+        got = so.cdf_keep_count(s, cand, tau)
+        near = np.abs(np.cumsum(np.sort(w)[::-1]) - tau).min() < 1e-9
+        assert got == best or near
+
+
+def test_cdf_keep_count_closed_forms():
+    cand = np.ones(10, dtype=bool)
+    s = np.zeros(10)                                   # uniform: p = 0.1 each
+    for tau, want in ((0.05, 1), (0.25, 3), (0.55, 6), (0.99, 10), (1.0, 10)):
+        assert so.cdf_keep_count(s, cand, tau) == want
+    s2 = np.array([math.log(9.0), 0, 0, 0, 0, 0, 0, 0, 0, 0])   # p = (0.5, 1/18 x 9)
+    assert so.cdf_keep_count(s2, cand, 0.4) == 1
+    assert so.cdf_keep_count(s2, cand, 0.5 + 1.5 / 18) == 3
+    assert so.cdf_keep_count(s2, ~cand, 0.5) == 0
+    r = np.random.default_rng(42)
+    s3 = r.standard_normal(50)
+    ks = [so.cdf_keep_count(s3, np.ones(50, bool), t) for t in np.linspace(0.01, 1.0, 60)]
+    assert ks[0] >= 1 and ks[-1] == 50 and all(a <= b for a, b in zip(ks, ks[1:]))
+
+
+def test_cdf_mask_keeps_the_ranked_prefix():
+    N, D = 1000, 64
+    q, k, _ = _drift_head(N, D, 43)
+    for causal in (False, True):
+        for tau in (0.3, 0.9):
+            mask, info = so.predict_mask(q, k, so.OracleParams(cdf=tau, causal=causal, theta=0.05))
+            S, valid, simk, simq = info["scores"], info["valid"], info["simk"], info["simq"]
+            for i in range(mask.shape[0]):
+                cand = valid[i] & simk
+                if not cand.any() or not simq[i]:
+                    continue
+                kept = np.flatnonzero(mask[i] & cand)
+                p = so.row_softmax(S[i], cand)
+                assert p[kept].sum() >= tau - 1e-12                 # the mass is reached
+                assert kept.size == info["kcount"][i]
+                rest = np.flatnonzero(cand & ~mask[i])
+                if rest.size:                                      # ... by the best blocks
+                    assert S[i][kept].min() >= S[i][rest].max()
+                    drop = p[kept].sum() - p[kept].min()
+                    assert drop < tau + 1e-12                      # and no block is spare
+
+
+def test_planted_cdf_off_by_one_is_caught(monkeypatch):
+    orig = so.cdf_keep_count
+
+    def bad(scores_row, cand, tau):
+        return max(0, orig(scores_row, cand, tau) - 1)
+    monkeypatch.setattr(so, "cdf_keep_count", bad)
+    with pytest.raises(AssertionError):
+        test_cdf_keep_count_closed_forms()
+
+
 def _drift_head(N, D, seed):
     r = np.random.default_rng(seed)
     nb = (N + 63) // 64
