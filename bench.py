@@ -83,7 +83,7 @@ def dense_equiv_ops(B, H, N, D, causal):
 class Path:
     """The hot path of one workload with preallocated outputs and workspace."""
 
-    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None, pv_fp8=None):
+    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None, pv_fp8=None, cdf=None):
         import torch
 
         import block_sparse_quantized_amd as bsq
@@ -92,6 +92,7 @@ class Path:
         self.qk_int8 = wl.qk_int8 if qk_int8 is None else qk_int8
         self.pv_fp16 = wl.pv_fp16 if pv_fp16 is None else pv_fp16
         self.pv_fp8 = wl.pv_fp8 if pv_fp8 is None else pv_fp8
+        self.cdf = cdf   # softmax-mass threshold of the threshold selection, or None (top-k)
         t0 = time.time()
         if inputs is None:
             self.q, self.k, self.v = synth.make_qkv(wl, device=dev)
@@ -123,6 +124,11 @@ class Path:
                                       qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
                                       pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
                                       prof=prof)
+        elif self.cdf is not None:
+            r = bsq.sparge_cdf_attn(q, k, v, self.cdf, wl.causal, filter_on=wl.filter_on,
+                                    qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                    pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
+                                    prof=prof)
         else:
             r = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
                                      qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
@@ -385,6 +391,17 @@ def main():
                 "roofline": roofline(st8, D, True, a8,
                                      committed_traffic(wl.name, kernel_src, "i8-qk/fp8-pv"), True)}
             del p8
+        if wl.api != "block_sparse":
+            # the threshold selection (softmax mass 0.95) on the same inputs and path
+            pc = Path(wl, dev, inputs=(path.q, path.k, path.v, path.mask), cdf=0.95)
+            _, stc = pc.step(stats=True)
+            sc, ac, prc = time_path(pc, ev, max(3, args.steps // 2), 1)
+            extras["cdf_select_variant"] = {
+                "cdf_threshold": 0.95, "ms_per_step": round(sc, 3),
+                "before_attention_ms": round(prc, 4), "attention_ms": round(ac, 4),
+                "tops_dense_equiv": round(dense / (sc * 1e-3) / 1e12, 2),
+                "kept_block_density": round(stc["kept_blocks"] / max(1, stc["valid_blocks"]), 4)}
+            del pc
         if wl.api != "block_sparse" and not wl.hilbert:
             pd = Path(synth.workload(wl.name, topk=1.0, filter_on=False), dev, qk_int8=False,
                       pv_fp16=False, inputs=(path.q, path.k, path.v, path.mask))

@@ -8,6 +8,7 @@ a GPU, the calls raise.
 
 Functions share the C names:
     sparge_topk_attn(q, k, v, topk=0.5, is_causal=False, ...)
+    sparge_cdf_attn(q, k, v, cdf_threshold, is_causal=False, ...)
     block_sparse_attn(q, k, v, mask_id=None, ...)
     sparge_predict_mask(q, k, topk, is_causal, ...)
     sparge_quantize_qk(q, k)
@@ -38,6 +39,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "sparge_topk_attn",
+    "sparge_cdf_attn",
     "block_sparse_attn",
     "sparge_predict_mask",
     "sparge_quantize_qk",
@@ -90,8 +92,21 @@ def _workspace(q: torch.Tensor, workspace: Optional[torch.Tensor]) -> Tuple[torc
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _head_array(vals, H: int, name: str):
+    """A host double array of H per-head values (kept alive by the caller), or None."""
+    if vals is None:
+        return None
+    vals = [float(x) for x in vals]
+    if len(vals) != H:
+        raise ValueError(f"{name} needs {H} values (one per head), got {len(vals)}")
+    return (ctypes.c_double * H)(*vals)
+
+
 def _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask_out, stats,
-          prof=None, pv_fp8=False):
+          prof=None, pv_fp8=False, heads=None):
+    """sparge_opts plus the stats struct; ``heads`` = (H, select, sim_threshold,
+    filter_lambda) per-head sequences (or None each); their ctypes arrays are kept on
+    the returned struct so they outlive the call."""
     o = SpargeOpts()
     lib().sparge_default_opts(ctypes.byref(o))
     o.scale = 0.0 if scale is None else float(scale)
@@ -106,6 +121,13 @@ def _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask
     o.stats = ctypes.pointer(st) if st is not None else None
     if prof is not None:  # raw hipEvent_t handles (start, attention begin, attention end)
         o.prof_start, o.prof_attn_begin, o.prof_attn_end = prof
+    if heads is not None:
+        H, sel, th, lam = heads
+        o._keep = [_head_array(sel, H, "head_select"), _head_array(th, H, "head_sim_threshold"),
+                   _head_array(lam, H, "head_filter_lambda")]
+        dbl = ctypes.POINTER(ctypes.c_double)
+        o.head_select, o.head_sim_threshold, o.head_filter_lambda = (
+            ctypes.cast(a, dbl) if a is not None else None for a in o._keep)
     return o, st
 
 
@@ -121,27 +143,19 @@ def _mask_shape(q: torch.Tensor):
     return (B, H, (N + 127) // 128, (N + 63) // 64)
 
 
-def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, scale=None,
-                     sim_threshold: float = 0.1, filter_lambda: float = -10.0,
-                     filter_on: bool = True, qk_int8: bool = False, pv_fp16: bool = False,
-                     pv_fp8: bool = False, return_mask: bool = False, stats: bool = False,
-                     out=None, workspace=None, prof=None):
-    """Sparse attention with the on-the-fly block-mask predictor (two-stage filter).
-
-    Returns ``out`` (same shape/dtype as q), plus the predicted uint8 block mask
-    when ``return_mask`` and a counters dict when ``stats`` (which synchronises).
-    """
+def _predicted_attn(fn, name, q, k, v, sel, is_causal, scale, sim_threshold, filter_lambda,
+                    filter_on, qk_int8, pv_fp16, pv_fp8, return_mask, stats, out, workspace, prof,
+                    head_select, head_sim_threshold, head_filter_lambda):
     if out is None:
         out = torch.empty_like(q)
     mask = torch.empty(_mask_shape(q), dtype=torch.uint8, device=q.device) if return_mask else None
     o, st = _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask, stats,
-                  prof, pv_fp8)
+                  prof, pv_fp8, (q.shape[1], head_select, head_sim_threshold, head_filter_lambda))
     ws, nbytes = _workspace(q, workspace)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
-    _check(lib().sparge_topk_attn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
-                                  ctypes.byref(do), ctypes.c_double(topk), int(bool(is_causal)),
-                                  ctypes.byref(o), ctypes.c_void_p(ws.data_ptr()),
-                                  ctypes.c_size_t(nbytes), _stream(q)), "sparge_topk_attn")
+    _check(fn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(do),
+              ctypes.c_double(sel), int(bool(is_causal)), ctypes.byref(o),
+              ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes), _stream(q)), name)
     res = [out]
     if return_mask:
         res.append(mask)
@@ -150,10 +164,43 @@ def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, sca
     return res[0] if len(res) == 1 else tuple(res)
 
 
+def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, scale=None,
+                     sim_threshold: float = 0.1, filter_lambda: float = -10.0,
+                     filter_on: bool = True, qk_int8: bool = False, pv_fp16: bool = False,
+                     pv_fp8: bool = False, return_mask: bool = False, stats: bool = False,
+                     out=None, workspace=None, prof=None, head_select=None,
+                     head_sim_threshold=None, head_filter_lambda=None):
+    """Sparse attention with the on-the-fly block-mask predictor (two-stage filter).
+
+    Returns ``out`` (same shape/dtype as q), plus the predicted uint8 block mask
+    when ``return_mask`` and a counters dict when ``stats`` (which synchronises).
+    ``head_*``: optional per-head sequences (H values) replacing topk,
+    sim_threshold and filter_lambda head by head.
+    """
+    return _predicted_attn(lib().sparge_topk_attn, "sparge_topk_attn", q, k, v, topk, is_causal,
+                           scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16,
+                           pv_fp8, return_mask, stats, out, workspace, prof, head_select,
+                           head_sim_threshold, head_filter_lambda)
+
+
+def sparge_cdf_attn(q, k, v, cdf_threshold: float, is_causal: bool = False, *, scale=None,
+                    sim_threshold: float = 0.1, filter_lambda: float = -10.0,
+                    filter_on: bool = True, qk_int8: bool = False, pv_fp16: bool = False,
+                    pv_fp8: bool = False, return_mask: bool = False, stats: bool = False,
+                    out=None, workspace=None, prof=None, head_select=None,
+                    head_sim_threshold=None, head_filter_lambda=None):
+    """Like ``sparge_topk_attn``, but each block row keeps the shortest ranked prefix of
+    its candidate blocks whose compressed-softmax mass reaches ``cdf_threshold``."""
+    return _predicted_attn(lib().sparge_cdf_attn, "sparge_cdf_attn", q, k, v, cdf_threshold,
+                           is_causal, scale, sim_threshold, filter_lambda, filter_on, qk_int8,
+                           pv_fp16, pv_fp8, return_mask, stats, out, workspace, prof, head_select,
+                           head_sim_threshold, head_filter_lambda)
+
+
 def block_sparse_attn(q, k, v, mask_id=None, *, scale=None, filter_lambda: float = -10.0,
                       filter_on: bool = False, qk_int8: bool = False, pv_fp16: bool = False,
                       pv_fp8: bool = False, stats: bool = False, out=None, workspace=None,
-                      prof=None):
+                      prof=None, head_filter_lambda=None):
     """Attention under a caller-given (B, H, ceil(N/128), ceil(N/64)) 0/1 block mask."""
     if out is None:
         out = torch.empty_like(q)
@@ -164,7 +211,7 @@ def block_sparse_attn(q, k, v, mask_id=None, *, scale=None, filter_lambda: float
         mask_id = mask_id.to(torch.uint8).contiguous()
         mptr = ctypes.c_void_p(mask_id.data_ptr())
     o, st = _opts(scale, 0.1, filter_lambda, filter_on, qk_int8, pv_fp16, None, stats, prof,
-                  pv_fp8)
+                  pv_fp8, (q.shape[1], None, None, head_filter_lambda))
     ws, nbytes = _workspace(q, workspace)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     _check(lib().block_sparse_attn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mptr,
@@ -174,10 +221,12 @@ def block_sparse_attn(q, k, v, mask_id=None, *, scale=None, filter_lambda: float
 
 
 def sparge_predict_mask(q, k, topk: float = 0.5, is_causal: bool = False, *, scale=None,
-                        sim_threshold: float = 0.1, stats: bool = False, workspace=None):
+                        sim_threshold: float = 0.1, stats: bool = False, workspace=None,
+                        head_select=None, head_sim_threshold=None):
     """Stage 1 only: the predicted (B, H, ceil(N/128), ceil(N/64)) uint8 block mask."""
     mask = torch.empty(_mask_shape(q), dtype=torch.uint8, device=q.device)
-    o, st = _opts(scale, sim_threshold, -10.0, True, False, False, None, stats)
+    o, st = _opts(scale, sim_threshold, -10.0, True, False, False, None, stats,
+                  heads=(q.shape[1], head_select, head_sim_threshold, None))
     ws, nbytes = _workspace(q, workspace)
     dq, dk = _desc(q, "q"), _desc(k, "k")
     _check(lib().sparge_predict_mask(ctypes.byref(dq), ctypes.byref(dk), ctypes.c_double(topk),

@@ -39,7 +39,10 @@ class SpargeOpts(ctypes.Structure):
                 ("qk_int8", ctypes.c_int32), ("pv_fp16", ctypes.c_int32),
                 ("pv_fp8", ctypes.c_int32), ("mask_out", ctypes.c_void_p),
                 ("stats", ctypes.POINTER(SpargeStats)), ("prof_start", ctypes.c_void_p),
-                ("prof_attn_begin", ctypes.c_void_p), ("prof_attn_end", ctypes.c_void_p)]
+                ("prof_attn_begin", ctypes.c_void_p), ("prof_attn_end", ctypes.c_void_p),
+                ("head_select", ctypes.POINTER(ctypes.c_double)),
+                ("head_sim_threshold", ctypes.POINTER(ctypes.c_double)),
+                ("head_filter_lambda", ctypes.POINTER(ctypes.c_double))]
 
 
 _P = ctypes.POINTER
@@ -53,6 +56,8 @@ PROTOTYPES = {
     "sparge_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i32, _P(SpargeOpts)]),
     "sparge_topk_attn": (_i32, [_T, _T, _T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp,
                                 ctypes.c_size_t, _vp]),
+    "sparge_cdf_attn": (_i32, [_T, _T, _T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp,
+                               ctypes.c_size_t, _vp]),
     "block_sparse_attn": (_i32, [_T, _T, _T, _vp, _T, _P(SpargeOpts), _vp, ctypes.c_size_t, _vp]),
     "sparge_predict_mask": (_i32, [_T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp, _vp,
                                    ctypes.c_size_t, _vp]),

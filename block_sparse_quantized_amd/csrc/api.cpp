@@ -35,6 +35,7 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.vmaxp = take(BH * d.nQ * d.D * sizeof(float));
   w.vscale = take(BH * d.D * sizeof(float));
   w.vinv = take(BH * d.D * sizeof(float));
+  w.hparams = take(3 * (size_t)d.H * sizeof(double));
   w.counters = take(8 * sizeof(unsigned long long));
   w.total = off;
   return w;
@@ -82,6 +83,17 @@ sparge_status check_opts(const sparge_opts* o) {
   return SPARGE_OK;
 }
 
+// The per-head arrays of opts (host memory, H values each).
+sparge_status check_head_params(const sparge_opts* o, int64_t H) {
+  if (!o) return SPARGE_OK;
+  for (int64_t h = 0; h < H; ++h) {
+    if (o->head_select && !(o->head_select[h] > 0.0 && o->head_select[h] <= 1.0)) return SPARGE_E_ARG;
+    if (o->head_sim_threshold && isnan(o->head_sim_threshold[h])) return SPARGE_E_ARG;
+    if (o->head_filter_lambda && !(o->head_filter_lambda[h] <= 0.0)) return SPARGE_E_ARG;
+  }
+  return SPARGE_OK;
+}
+
 sparge_status check_qkv(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
                         const sparge_tensor* out) {
   sparge_status st;
@@ -104,6 +116,10 @@ struct Ctx {
   char* ws;
   hipStream_t s;
   unsigned long long* counters;  // nullable
+  // device copies of the per-head arrays (nullable)
+  const double* head_sel = nullptr;
+  const double* head_theta = nullptr;
+  const double* head_lambda = nullptr;
   template <typename T>
   T* at(size_t off) const { return (T*)(ws + off); }
 };
@@ -116,6 +132,22 @@ sparge_status begin_stats(Ctx& c, const sparge_opts* o) {
   if (o && o->stats) {
     c.counters = c.at<unsigned long long>(c.w.counters);
     SPARGE_TRY(hipMemsetAsync(c.counters, 0, 8 * sizeof(unsigned long long), c.s));
+  }
+  return SPARGE_OK;
+}
+
+// Copies the caller's per-head arrays into the workspace (pageable host memory:
+// the copy has consumed the source when the call returns).
+sparge_status stage_head_params(Ctx& c, const sparge_opts& o) {
+  double* dst = c.at<double>(c.w.hparams);
+  const size_t bytes = (size_t)c.d.H * sizeof(double);
+  const double* src[3] = {o.head_select, o.head_sim_threshold, o.head_filter_lambda};
+  const double** out[3] = {&c.head_sel, &c.head_theta, &c.head_lambda};
+  for (int a = 0; a < 3; ++a) {
+    *out[a] = nullptr;
+    if (!src[a]) continue;
+    SPARGE_TRY(hipMemcpyAsync(dst + a * c.d.H, src[a], bytes, hipMemcpyHostToDevice, c.s));
+    *out[a] = dst + a * c.d.H;
   }
   return SPARGE_OK;
 }
@@ -197,6 +229,7 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
   const double log2e = 1.4426950408889634;
   p.c = (float)(scale * log2e);
   p.lam2 = (float)(o.filter_lambda * log2e);
+  p.head_lambda = c.head_lambda;
   p.lists = c.at<uint16_t>(c.w.lists);
   p.counts = c.at<int>(c.w.counts);
   p.counters = c.counters;
@@ -217,8 +250,18 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
   return SPARGE_OK;
 }
 
+SelectParams select_params(const Ctx& c, double sel, int cdf, const sparge_opts& o) {
+  SelectParams sp;
+  sp.sel = sel;
+  sp.theta = o.sim_threshold;
+  sp.head_sel = c.head_sel;
+  sp.head_theta = c.head_theta;
+  sp.cdf = cdf;
+  return sp;
+}
+
 sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor* k, double topk,
-                            int causal, const sparge_opts& o, uint8_t* mask_out) {
+                            int cdf, int causal, const sparge_opts& o, uint8_t* mask_out) {
   const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
   double* qmean = c.at<double>(c.w.qmean);
   double* qsim = c.at<double>(c.w.qsim);
@@ -227,7 +270,7 @@ sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor*
   double* scores = c.at<double>(c.w.scores);
   SPARGE_TRY(launch_block_stats(view_of(q), view_of(k), q->dtype, c.d, qmean, qsim, kmean, ksim, c.s));
   SPARGE_TRY(launch_pooled_scores(qmean, kmean, c.d, causal, scale, scores, c.s));
-  SPARGE_TRY(launch_select(scores, qsim, ksim, c.d, causal, topk, o.sim_threshold, mask_out,
+  SPARGE_TRY(launch_select(scores, qsim, ksim, c.d, causal, select_params(c, topk, cdf, o), mask_out,
                            c.at<uint16_t>(c.w.lists), c.at<int>(c.w.counts), c.counters, c.s));
   return SPARGE_OK;
 }
@@ -267,13 +310,13 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
 }
 
 // Pooled scores and selection from the block statistics already in the workspace.
-sparge_status run_select(Ctx& c, double topk, int causal, const sparge_opts& o) {
+sparge_status run_select(Ctx& c, double topk, int cdf, int causal, const sparge_opts& o) {
   const double scale = o.scale > 0.0 ? o.scale : 1.0 / sqrt((double)c.d.D);
   double* scores = c.at<double>(c.w.scores);
   SPARGE_TRY(launch_pooled_scores(c.at<double>(c.w.qmean), c.at<double>(c.w.kmean), c.d, causal,
                                   scale, scores, c.s));
   SPARGE_TRY(launch_select(scores, c.at<double>(c.w.qsim), c.at<double>(c.w.ksim), c.d, causal,
-                           topk, o.sim_threshold, o.mask_out, c.at<uint16_t>(c.w.lists),
+                           select_params(c, topk, cdf, o), o.mask_out, c.at<uint16_t>(c.w.lists),
                            c.at<int>(c.w.counts), c.counters, c.s));
   return SPARGE_OK;
 }
@@ -315,31 +358,58 @@ size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
   return plan_workspace(make_dims((int)B, (int)H, (int)N, (int)D), dtype).total;
 }
 
-sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
-                               const sparge_tensor* v, const sparge_tensor* out, double topk,
-                               int32_t is_causal, const sparge_opts* opts, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// sparge_topk_attn (cdf = 0: sel is the kept fraction) and sparge_cdf_attn (cdf = 1:
+// sel is the softmax-mass threshold).
+sparge_status predicted_attn(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
+                             const sparge_tensor* out, double sel, int cdf, int32_t is_causal,
+                             const sparge_opts* opts, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   sparge_status st;
   if ((st = check_qkv(q, k, v, out)) != SPARGE_OK) return st;
   if ((st = check_opts(opts)) != SPARGE_OK) return st;
-  if (!(topk > 0.0 && topk <= 1.0)) return SPARGE_E_ARG;
+  if ((st = check_head_params(opts, q->H)) != SPARGE_OK) return st;
+  if (!(sel > 0.0 && sel <= 1.0)) return SPARGE_E_ARG;
   sparge_opts o;
   if (opts) o = *opts; else sparge_default_opts(&o);
   if (o.pv_fp8 && q->dtype == SPARGE_F32) return SPARGE_E_UNSUPPORTED;
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  if ((st = stage_head_params(c, o)) != SPARGE_OK) return st;
   Operands op;
   if (q->dtype != SPARGE_F32) {
     if ((st = prep16(c, q, k, v, o, op)) != SPARGE_OK) return st;
-    if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
+    if ((st = run_select(c, sel, cdf, is_causal != 0, o)) != SPARGE_OK) return st;
     if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0, true)) != SPARGE_OK) return st;
     return end_stats(c, &o);
   }
   if ((st = prepare_operands(c, q, k, v, o.pv_fp16, op)) != SPARGE_OK) return st;
-  if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
+  if ((st = run_predictor(c, q, k, sel, cdf, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
   if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0)) != SPARGE_OK) return st;
   return end_stats(c, &o);
+}
+
+}  // namespace
+
+extern "C" {
+
+sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
+                               const sparge_tensor* v, const sparge_tensor* out, double topk,
+                               int32_t is_causal, const sparge_opts* opts, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return predicted_attn(q, k, v, out, topk, 0, is_causal, opts, workspace, workspace_bytes, stream);
+}
+
+sparge_status sparge_cdf_attn(const sparge_tensor* q, const sparge_tensor* k,
+                              const sparge_tensor* v, const sparge_tensor* out,
+                              double cdf_threshold, int32_t is_causal, const sparge_opts* opts,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return predicted_attn(q, k, v, out, cdf_threshold, 1, is_causal, opts, workspace,
+                        workspace_bytes, stream);
 }
 
 sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
@@ -357,9 +427,13 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
     o.filter_on = 0;
   }
   if (o.pv_fp8 && q->dtype == SPARGE_F32) return SPARGE_E_UNSUPPORTED;
+  if ((st = check_head_params(&o, q->H)) != SPARGE_OK) return st;
+  o.head_select = nullptr;          // no selection here
+  o.head_sim_threshold = nullptr;
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  if ((st = stage_head_params(c, o)) != SPARGE_OK) return st;
   Operands op;
   bool k_ready = false;
   const int v_conv = v->dtype == SPARGE_BF16 && o.pv_fp16;
@@ -384,21 +458,24 @@ sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k
   if ((st = check_opts(opts)) != SPARGE_OK) return st;
   if (!mask_out) return SPARGE_E_NULL;
   if (!(topk > 0.0 && topk <= 1.0)) return SPARGE_E_ARG;
+  if ((st = check_head_params(opts, q->H)) != SPARGE_OK) return st;
   sparge_opts o;
   if (opts) o = *opts; else sparge_default_opts(&o);
+  o.head_filter_lambda = nullptr;   // no attention here
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
+  if ((st = stage_head_params(c, o)) != SPARGE_OK) return st;
   if (q->dtype != SPARGE_F32) {
     // the statistics of the fused pass the attention path uses (no int8 K, no V)
     SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), q->dtype, c.d, c.at<double>(c.w.qmean),
                            c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                            nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, c.s));
     o.mask_out = mask_out;
-    if ((st = run_select(c, topk, is_causal != 0, o)) != SPARGE_OK) return st;
+    if ((st = run_select(c, topk, 0, is_causal != 0, o)) != SPARGE_OK) return st;
     return end_stats(c, &o);
   }
-  if ((st = run_predictor(c, q, k, topk, is_causal != 0, o, mask_out)) != SPARGE_OK) return st;
+  if ((st = run_predictor(c, q, k, topk, 0, is_causal != 0, o, mask_out)) != SPARGE_OK) return st;
   return end_stats(c, &o);
 }
 
@@ -464,6 +541,6 @@ const char* sparge_status_str(int32_t s) {
   }
 }
 
-int32_t sparge_abi_version(void) { return 2; }
+int32_t sparge_abi_version(void) { return 3; }
 
 }  // extern "C"

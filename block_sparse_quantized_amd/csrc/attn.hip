@@ -232,6 +232,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const int i = p.causal ? (d.nQ - 1 - ii) : ii;
   const int b = bh / d.H, h = bh - b * d.H;
   const int N = d.N;
+  // filter threshold in log2 units, per head when the caller gave per-head values
+  const float lam2 = p.head_lambda ? (float)(p.head_lambda[h] * 1.4426950408889634) : p.lam2;
   const int wrow0 = i * 128 + w * 32;
   const int t = wrow0 + ql;
   const bool row_ok = t < N;
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     bool skip = false;
     if (p.filter_on) {
       const float m_new = fmaxf(m_true, mx);
-      const bool keep = (mx != kNegInf) && (mx - m_new >= p.lam2);
+      const bool keep = (mx != kNegInf) && (mx - m_new >= lam2);
       if (__ballot(keep) == 0ull) {
         ++n_skip;
         skip = true;

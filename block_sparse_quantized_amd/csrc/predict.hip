@@ -12,6 +12,8 @@
 //     plus every valid block of a non-similar row or column.
 // All arithmetic that decides the mask runs in IEEE fp64 with no fused
 // multiply-adds outside the dot products, following the reference steps.
+#include <type_traits>
+
 #include "sparge_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -210,18 +212,56 @@ __device__ __forceinline__ int keep_count(int C, double topk) {
 // are written in ascending order (ballots, then a prefix over the four waves).
 constexpr int kSelMaxM = 16;  // keys per thread: nK <= 4096
 
+// LDS of the threshold selection: the row's candidates as (order key, block index)
+// pairs, ranked by a bitonic sort.
+struct CdfLds {
+  unsigned long long key[kSelMaxM * 256];
+  unsigned short j[kSelMaxM * 256];
+  double part[4];
+  int cnt[4];
+};
+
+// a ranks before b: larger score first, then the lower block index
+__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ja, unsigned long long kb, int jb) {
+  return ka > kb || (ka == kb && ja < jb);
+}
+
+// Block-wide exclusive prefix of one double per thread, in thread order (fixed
+// association: a wavefront scan, then the four wavefront totals in order); also
+// returns the total.  Every thread must call it.
+__device__ double block_excl_scan(double x, double* part, double& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  double incl = x;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) part[wv] = incl;
+  __syncthreads();
+  double before = 0.0;
+  for (int w2 = 0; w2 < wv; ++w2) before += part[w2];
+  total = ((part[0] + part[1]) + part[2]) + part[3];
+  __syncthreads();
+  return before + (incl - x);
+}
+
+template <bool CDF>
 __global__ __launch_bounds__(256) void select_kernel(const double* scores, const double* qsim,
                                                      const double* ksim, Dims d, int causal,
-                                                     double topk, double theta, uint8_t* mask_out,
+                                                     SelectParams sp, uint8_t* mask_out,
                                                      uint16_t* lists, int* counts,
                                                      unsigned long long* counters) {
   __shared__ unsigned int hist[256];
   __shared__ int sh_int[4][2];
   __shared__ int sh_sel[2];
   __shared__ unsigned long long sh_key;
+  __shared__ std::conditional_t<CDF, CdfLds, char> cdf_lds;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.x;
   const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
+  const int h = bh % d.H;
+  const double theta = sp.head_theta ? sp.head_theta[h] : sp.theta;
+  const double sel = sp.head_sel ? sp.head_sel[h] : sp.sel;
   const int nK = d.nK;
   const int mk = (nK + 255) >> 8;
   const int jv = causal ? min(nK, 2 * i + 2) : nK;
@@ -260,10 +300,87 @@ __global__ __launch_bounds__(256) void select_kernel(const double* scores, const
   if (lane == 0) sh_int[wv][0] = cand_local;
   __syncthreads();
   const int C = sh_int[0][0] + sh_int[1][0] + sh_int[2][0] + sh_int[3][0];
-  const int kk = keep_count(C, topk);
+  __syncthreads();   // sh_int is reused below
   unsigned long long T = 0ull, pmask = 0ull;
   int need = 0;
-  if (kk > 0) {
+  int kk;
+  if constexpr (CDF) {
+    kk = 0;
+    if (C > 0) {
+      // rank the candidates: bitonic sort of (key, j) over the first n2 >= jv slots
+      // (non-candidates and padding carry key 0 and sort last)
+      CdfLds& L = cdf_lds;
+      int n2 = 64;
+      while (n2 < jv) n2 <<= 1;
+      for (int m = tid; m < n2; m += 256) {   // slot m starts as block m
+        L.key[m] = 0ull;
+        L.j[m] = (unsigned short)m;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < kSelMaxM; ++m) {
+        const int j = tid + 256 * m;
+        if (((candm >> m) & 1u)) L.key[j] = key[m];
+      }
+      __syncthreads();
+      for (int kb = 2; kb <= n2; kb <<= 1) {
+        for (int jj = kb >> 1; jj > 0; jj >>= 1) {
+          for (int idx = tid; idx < (n2 >> 1); idx += 256) {
+            const int a = 2 * jj * (idx / jj) + (idx % jj), b = a + jj;
+            const unsigned long long ka = L.key[a], kb2 = L.key[b];
+            const int ja = L.j[a], jb = L.j[b];
+            const bool a_first = ranks_before(ka, ja, kb2, jb);
+            const bool up = (a & kb) == 0;   // this run is ordered best-first
+            if (up ? !a_first : a_first) {
+              L.key[a] = kb2;
+              L.key[b] = ka;
+              L.j[a] = (unsigned short)jb;
+              L.j[b] = (unsigned short)ja;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // softmax weights e_m = exp(s_(m) - s_(0)) of the first C ranks, a prefix sum
+      // in rank order (thread t owns ranks 16t .. 16t+15), and the count of ranks
+      // whose cumulative weight stays below tau * total
+      const double smax = srow[L.j[0]];
+      double e[kSelMaxM], run = 0.0;
+#pragma unroll
+      for (int m = 0; m < kSelMaxM; ++m) {
+        const int r = kSelMaxM * tid + m;
+        e[m] = r < C ? exp(srow[L.j[r]] - smax) : 0.0;
+        run += e[m];
+      }
+      double total;
+      double pre = block_excl_scan(run, L.part, total);
+      const double lim = sel * total;
+      int below = 0;
+#pragma unroll
+      for (int m = 0; m < kSelMaxM; ++m) {
+        const int r = kSelMaxM * tid + m;
+        pre += e[m];
+        below += (r < C && pre < lim) ? 1 : 0;
+      }
+      for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, 64);
+      if (lane == 0) L.cnt[wv] = below;
+      __syncthreads();
+      kk = min(C, 1 + L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3]);
+      // the threshold key and how many of the equal keys the prefix takes
+      T = L.key[kk - 1];
+      int eq = 0;
+      for (int r = tid; r < kk; r += 256) eq += (L.key[r] == T) ? 1 : 0;
+      for (int off = 32; off >= 1; off >>= 1) eq += __shfl_xor(eq, off, 64);
+      __syncthreads();
+      if (lane == 0) L.cnt[wv] = eq;
+      __syncthreads();
+      need = L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3];
+      __syncthreads();
+    }
+  } else {
+    kk = keep_count(C, sel);
+  }
+  if (!CDF && kk > 0) {
     int krem = kk;  // rank still to be located among keys matching the prefix
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
@@ -474,13 +591,17 @@ hipError_t launch_pooled_scores(const double* qmean, const double* kmean, const 
 }
 
 hipError_t launch_select(const double* scores, const double* qsim, const double* ksim,
-                         const Dims& d, int causal, double topk, double theta, uint8_t* mask_out,
+                         const Dims& d, int causal, const SelectParams& sp, uint8_t* mask_out,
                          uint16_t* lists, int* counts, unsigned long long* counters,
                          hipStream_t s) {
   if (d.nK > 256 * kSelMaxM) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
-  select_kernel<<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, topk, theta, mask_out, lists,
-                                     counts, counters);
+  if (sp.cdf)
+    select_kernel<true><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists,
+                                             counts, counters);
+  else
+    select_kernel<false><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists,
+                                              counts, counters);
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct Workspace {
                                    // with fp8 P.V (16-bit inputs only) the E4M3 V tiles
   size_t vmaxp, vscale, vinv;      // fp8 P.V: per-block channel max |v| (BH, nQ, D), fp32
                                    // channel scales and inverses (BH, D)
+  size_t hparams;                  // per-head knobs (3 x H fp64): selection, theta, lambda
   size_t counters;                 // 8 x uint64 stats counters
   size_t total;
 };
@@ -74,8 +75,18 @@ hipError_t launch_pooled_scores(const double* qmean, const double* kmean, const 
                                 int causal, double scale, double* scores, hipStream_t s);
 
 // Per block row: similarity gate, top-k selection, mask row and kept-block list.
+// Selection knobs: the scalar values, optionally replaced per head h by device
+// arrays of H values.
+struct SelectParams {
+  double sel;                 // topk fraction, or the softmax-mass threshold when cdf
+  double theta;               // self-similarity threshold
+  const double* head_sel;     // nullable (H)
+  const double* head_theta;   // nullable (H)
+  int cdf;                    // 1: keep the shortest ranked prefix reaching mass sel
+};
+
 hipError_t launch_select(const double* scores, const double* qsim, const double* ksim,
-                         const Dims& d, int causal, double topk, double theta,
+                         const Dims& d, int causal, const SelectParams& sp,
                          uint8_t* mask_out, uint16_t* lists, int* counts,
                          unsigned long long* counters, hipStream_t s);
 
@@ -124,6 +135,7 @@ struct AttnParams {
   const int8_t* k8;      // int8 path: codes, (BH, nK*64, D)
   const float* kscale;   // (BH, nK)
   const float* kbar;     // (BH, nK, D)
+  const double* head_lambda; // nullable (H): per-head filter lambda (natural-log units)
   const unsigned char* v8t;  // fp8 P.V: E4M3 V tiles (BH, nK, D, 64)
   const float* vscale;       // fp8 P.V: channel scales (BH, D)
   unsigned long long* counters;  // nullable: [2] = group updates, [3] = skipped updates

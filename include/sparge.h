@@ -104,13 +104,22 @@ typedef struct {
   void* prof_attn_begin; /* optional hipEvent_t recorded right before the attention
                             kernel's launch */
   void* prof_attn_end;   /* optional hipEvent_t recorded right after it */
+  /* Per-head knobs ([chapterpal] recommendations: calibrate the thresholds per layer
+   * and attention head).  Each is an optional HOST array of H values (H of the
+   * call's tensors, shared by every batch entry) that replaces the scalar for head
+   * h; NULL keeps the scalar.  Values are validated like the scalars (SPARGE_E_ARG)
+   * and copied into the workspace before the call returns. */
+  const double* head_select;        /* topk of sparge_topk_attn / sparge_predict_mask,
+                                       cdf_threshold of sparge_cdf_attn: each in (0, 1] */
+  const double* head_sim_threshold; /* theta per head (not NaN) */
+  const double* head_filter_lambda; /* lambda per head (<= 0, not NaN) */
 } sparge_opts;
 
 /* Fills *opts with the defaults listed above (filter_on = 1). */
 void sparge_default_opts(sparge_opts* opts);
 
-/* Workspace bytes that sparge_topk_attn, block_sparse_attn, sparge_predict_mask
- * and sparge_quantize_qk need for tensors of this shape and dtype under `opts`
+/* Workspace bytes that sparge_topk_attn, sparge_cdf_attn, block_sparse_attn,
+ * sparge_predict_mask and sparge_quantize_qk need for tensors of this shape and dtype under `opts`
  * (NULL = defaults).  Returns 0 when the shape or dtype is invalid.  The value
  * is an upper bound for every entry point, so one workspace serves them all. */
 size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t dtype,
@@ -130,11 +139,26 @@ sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
                                double topk, int32_t is_causal, const sparge_opts* opts,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Threshold variant of sparge_topk_attn (the meansim calls without topk, e.g.
+ * spas_sage2_attn_meansim_cuda of [readme] "Avalible API" and [gittools] API list;
+ * [chapterpal] recommendations on calibrating thresholds): identical except for the
+ * per-row selection, which keeps the shortest prefix of the row's candidate blocks,
+ * ranked by compressed score (descending, lower block index first on ties), whose
+ * share of the row softmax of the compressed map (fp64, over the candidates)
+ * reaches cdf_threshold; at least one candidate is kept.  cdf_threshold must lie in
+ * (0, 1] (else SPARGE_E_ARG); opts->head_select gives it per head. */
+sparge_status sparge_cdf_attn(const sparge_tensor* q, const sparge_tensor* k,
+                              const sparge_tensor* v, const sparge_tensor* out,
+                              double cdf_threshold, int32_t is_causal, const sparge_opts* opts,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Attention under a caller-given block mask: block_sparse_sage2_attn_cuda(q, k,
  * v, mask_id) of [gittools] custom block-sparse mask section; [topgit]
  * "Strengths".  mask_id: device uint8 (B, H, ceil(N/128), ceil(N/64)), contiguous;
  * nonzero keeps the 128x64 block; NULL keeps every block.  Not causal (the call
- * has no is_causal argument).  A query row with no kept block outputs zeros. */
+ * has no is_causal argument).  A query row with no kept block outputs zeros.
+ * opts->head_filter_lambda applies; head_select and head_sim_threshold are
+ * ignored. */
 sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
                                 const sparge_tensor* v, const uint8_t* mask_id,
                                 const sparge_tensor* out, const sparge_opts* opts,
@@ -142,7 +166,8 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
 
 /* Stage 1 only: writes the predicted block mask to mask_out (device uint8,
  * (B, H, ceil(N/128), ceil(N/64)), contiguous).  Same arguments and rules as
- * sparge_topk_attn; opts->mask_out is ignored. */
+ * sparge_topk_attn; opts->mask_out is ignored.  With opts->head_select the topk
+ * argument is replaced per head; head_filter_lambda is ignored. */
 sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k, double topk,
                                   int32_t is_causal, const sparge_opts* opts, uint8_t* mask_out,
                                   void* workspace, size_t workspace_bytes, void* stream);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     missing = [n for n in names if n not in exported]
     assert not missing, f"declared but not exported: {missing}"
     assert set(names) == set(L.PROTOTYPES), "binding prototypes must cover exactly the header"
-    assert lib.sparge_abi_version() == 2
+    assert lib.sparge_abi_version() == 3
 
 
 def test_struct_layout_matches_c_compiler():
@@ -112,6 +112,44 @@ def test_validation_errors_topk(lib):
     r = lib.block_sparse_attn(*(ctypes.byref(t) for t in f32[:3]), None, ctypes.byref(f32[3]),
                               ctypes.byref(bad), FAKE, 1 << 40, None)
     assert r == -5
+
+
+def call_cdf(lib, q, k, v, o, tau=0.9, opts=None):
+    return lib.sparge_cdf_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                               tau, 0, opts, FAKE, 1 << 40, None)
+
+
+def test_validation_errors_cdf_and_per_head_knobs(lib):
+    q, k, v, o = T(), T(data=FAKE + 4096), T(data=FAKE + 8192), T(data=FAKE + 12288)
+    for tau in (0.0, -0.5, 1.5, float("nan")):
+        assert call_cdf(lib, q, k, v, o, tau) == -4
+    H = q.H
+    dbl = ctypes.POINTER(ctypes.c_double)
+
+    def opts_with(**arrays):
+        op = L.SpargeOpts()
+        lib.sparge_default_opts(ctypes.byref(op))
+        keep = []
+        for name, vals in arrays.items():
+            a = (ctypes.c_double * H)(*vals)
+            keep.append(a)
+            setattr(op, name, ctypes.cast(a, dbl))
+        return op, keep
+    # every check happens on the host before anything touches the (fake) device memory
+    for name, vals in (("head_select", [0.5, 0.0]), ("head_select", [1.2, 0.5]),
+                       ("head_sim_threshold", [0.1, float("nan")]),
+                       ("head_filter_lambda", [-10.0, 0.5]), ("head_filter_lambda", [float("nan"), -1.0])):
+        op, keep = opts_with(**{name: vals})
+        assert call_topk(lib, q, k, v, o, opts=ctypes.byref(op)) == -4, (name, vals)
+        assert call_cdf(lib, q, k, v, o, 0.9, opts=ctypes.byref(op)) == -4, (name, vals)
+    op, keep = opts_with(head_filter_lambda=[-10.0, 0.5])
+    r = lib.block_sparse_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, ctypes.byref(o),
+                              ctypes.byref(op), FAKE, 1 << 40, None)
+    assert r == -4
+    op, keep = opts_with(head_select=[0.5, 2.0])
+    r = lib.sparge_predict_mask(ctypes.byref(q), ctypes.byref(k), 0.5, 1, ctypes.byref(op), FAKE,
+                                FAKE, 1 << 40, None)
+    assert r == -4
 
 
 def test_validation_errors_other_entry_points(lib):

@@ -375,6 +375,106 @@ def test_fp8_pv_fp32_inputs_unsupported(dev):
                              pv_fp8=True, pv_fp16=True)
 
 
+# ------------------------------------------- threshold selection, per-head knobs
+
+def cdf_mismatches(gpu_mask, om, infos, tau, theta=0.1):
+    """Unexcused mask mismatches under the threshold selection: a row may differ only
+    when the GPU kept the oracle's ranked prefix of a length that the oracle's
+    cumulative masses allow within 1e-9 of tau, or by the top-k near-tie rule."""
+    B, H, nQ, nK = om.shape
+    g = gpu_mask.reshape(B * H, nQ, nK).astype(bool)
+    o = om.reshape(B * H, nQ, nK)
+    bad = 0
+    for bh in range(B * H):
+        info = infos[bh]
+        S, valid, simk = info["scores"], info["valid"], info["simk"]
+        t = tau[bh % H] if np.ndim(tau) else tau
+        for i in np.flatnonzero((g[bh] != o[bh]).any(axis=1)):
+            cand = valid[i] & simk
+            js = np.flatnonzero(cand)
+            order = np.lexsort((js, -S[i][js]))
+            e = np.exp(S[i][js][order] - S[i][js].max())
+            cum = np.cumsum(e / e.sum())
+            lo = min(js.size, 1 + int((cum < t - 1e-9).sum()))
+            hi = min(js.size, 1 + int((cum < t + 1e-9).sum()))
+            kg = int((g[bh][i] & cand).sum())
+            row = valid[i] & (~info["simq"][i] | ~simk)
+            row[so.select_row(S[i], cand, kg)] = True
+            if not (lo <= kg <= hi and np.array_equal(row, g[bh][i])):
+                bad += 1
+    return bad
+
+
+@pytest.mark.parametrize("N,D,causal,tau,theta", [
+    (1000, 128, True, 0.9, 0.1), (1500, 64, False, 0.5, 0.0), (129, 128, True, 0.99, 0.0),
+    (4000, 128, True, 0.3, 0.1), (3000, 64, False, 0.8, 0.0), (5000, 128, True, 0.95, 0.0)])
+def test_cdf_selection_matches_oracle(dev, N, D, causal, tau, theta):
+    # theta = 0 makes every block similar, so every valid block competes
+    wl = synth.workload("llm8k", H=3, N=N, D=D)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    out, gm = bsq.sparge_cdf_attn(q, k, v, tau, causal, filter_on=True, return_mask=True,
+                                  sim_threshold=theta)
+    torch.cuda.synchronize()
+    om, infos = oracle_predict(q, k, so.OracleParams(cdf=tau, causal=causal, theta=theta))
+    g = gm.cpu().numpy().astype(bool)
+    bad = cdf_mismatches(g, om, infos, tau, theta)
+    same = (g == om).all(axis=3)
+    say(f"cdf N={N} D={D} causal={causal} tau={tau} theta={theta}: unexcused {bad}, rows "
+        f"differing {int((~same).sum())}, density {om.mean():.3f}")
+    assert bad == 0
+    rows = np.repeat(same, so.BQ, axis=2)[:, :, :N]
+    ref, _ = oracle_outputs(q, k, v, om, causal, lam=-10.0)
+    err = np.abs(f64(out) - ref)[rows].max()
+    say(f"  output err {err:.3e}")
+    assert err < TOL16
+
+
+def test_per_head_knobs(dev):
+    B, H, N, D = 1, 4, 1200, 128
+    wl = synth.workload("llm8k", H=H, N=N, D=D)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    sel = [0.2, 0.5, 0.8, 1.0]
+    theta = [0.05, 0.1, 0.3, 0.1]
+    lam = [-10.0, -3.0, -float("inf"), -20.0]
+    out, gm, st = bsq.sparge_topk_attn(q, k, v, 0.5, True, head_select=sel, head_sim_threshold=theta,
+                                       head_filter_lambda=lam, return_mask=True, stats=True)
+    g = gm.cpu().numpy().astype(bool)
+    qn, kn, vn = f64(q), f64(k), f64(v)
+    skipped = 0
+    for h in range(H):
+        p = so.OracleParams(topk=sel[h], causal=True, theta=theta[h])
+        m, info = so.predict_mask(qn[0, h], kn[0, h], p)
+        bad, _ = unexcused_mismatches(g[:, h:h + 1], m[None, None], [info], theta=theta[h])
+        assert bad == 0
+        rows = np.repeat((g[0, h] == m).all(axis=1), so.BQ)[:N]
+        o, sk = so.attend_head(qn[0, h], kn[0, h], vn[0, h], m, True, lam=lam[h], return_skips=True)
+        skipped += sum(len(x) for x in sk.values())
+        err = np.abs(f64(out)[0, h] - o)[rows].max()
+        say(f"per-head knobs head {h}: topk {sel[h]} theta {theta[h]} lambda {lam[h]}: err {err:.3e}")
+        assert err < TOL16
+    say(f"  skipped updates gpu {st['skipped_updates']} oracle {skipped}")
+    assert st["skipped_updates"] == skipped
+    # equal per-head values reproduce the scalar call exactly
+    a = bsq.sparge_topk_attn(q, k, v, 0.3, True, sim_threshold=0.2, filter_lambda=-5.0)
+    b = bsq.sparge_topk_attn(q, k, v, 0.7, True, head_select=[0.3] * H, head_sim_threshold=[0.2] * H,
+                             head_filter_lambda=[-5.0] * H)
+    assert torch.equal(a, b)
+    # per-head cdf thresholds
+    taus = [0.5, 0.9, 0.99, 0.3]
+    out2, gm2 = bsq.sparge_cdf_attn(q, k, v, 0.9, True, head_select=taus, return_mask=True)
+    for h in range(H):
+        m, info = so.predict_mask(qn[0, h], kn[0, h], so.OracleParams(cdf=taus[h], causal=True))
+        assert cdf_mismatches(gm2.cpu().numpy()[:, h:h + 1], m[None, None], [info], taus[h]) == 0
+    # block_sparse_attn takes the per-head lambda
+    nQ, nK = so.num_blocks(N)
+    mask = (torch.rand((B, H, nQ, nK), generator=torch.Generator().manual_seed(3)) < 0.6).to(torch.uint8)
+    out3 = bsq.block_sparse_attn(q, k, v, mask.to(dev), filter_on=True, head_filter_lambda=lam)
+    for h in range(H):
+        o = so.attend_head(qn[0, h], kn[0, h], vn[0, h], mask[0, h].numpy().astype(bool), False,
+                           lam=lam[h])
+        assert np.abs(f64(out3)[0, h] - o).max() < TOL16
+
+
 # -------------------------------------------------------------- Hilbert reorder
 
 def test_reorder_gather_scatter(dev):
