@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
 import hashlib
 import json
 import math
@@ -195,18 +196,17 @@ def path_dtype(qk_int8, pv_fp16, pv_fp8):
 
 def committed_traffic(wl_name, kernel_src, dtype):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary of this
-    workload and path, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"sparse_attn_{wl_name}_traffic.json")
-    if not os.path.exists(path):
-        return None
+    workload and path (profiles/sparse_attn_<workload>*_traffic.json), if it was
+    taken on the current kernel source; else None."""
     try:
-        rec = json.load(open(path))
         sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha or rec.get("path", dtype) != dtype:
-            return None
-        return rec.get("hbm_bytes_per_launch")
+        for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"sparse_attn_{wl_name}*_traffic.json"))):
+            rec = json.load(open(path))
+            if rec.get("path") == dtype and rec.get("kernel_source_sha256") == sha:
+                return rec.get("hbm_bytes_per_launch")
     except Exception:
         return None
+    return None
 
 
 def cpu_baseline(wl, q, k, v, budget_s=20.0):
@@ -327,6 +327,10 @@ def main():
     ap.add_argument("--workload", default="llm128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--pv-fp8", action="store_true",
+                    help="time the int8 Q.K^T / fp8 P.V path of the workload instead of its own")
+    ap.add_argument("--cdf", type=float, default=None, metavar="TAU",
+                    help="time the threshold selection (softmax mass TAU) instead of top-k")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -356,7 +360,10 @@ def main():
     log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D} steps={args.steps} "
         f"warmup={args.warmup}")
 
-    path = Path(wl, dev)
+    if args.pv_fp8:
+        path = Path(wl, dev, qk_int8=True, pv_fp16=False, pv_fp8=True, cdf=args.cdf)
+    else:
+        path = Path(wl, dev, cdf=args.cdf)
     _, stats = path.step(stats=True)
     torch.cuda.synchronize()
     ms_step, ms_attn, ms_pre = time_path(path, ev, args.steps, args.warmup)
@@ -439,7 +446,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "causal": wl.causal,
                    "topk": wl.topk if wl.api != "block_sparse" else None, "api": wl.api,
                    "filter_on": wl.filter_on, "qk_int8": path.qk_int8, "pv_fp16": path.pv_fp16,
-                   "pv_fp8": path.pv_fp8,
+                   "pv_fp8": path.pv_fp8, "cdf_threshold": path.cdf,
                    "hilbert": wl.hilbert},
         "roofline": roof,
         "cpu_baseline": cpu,

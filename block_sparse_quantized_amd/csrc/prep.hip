@@ -319,15 +319,29 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
 
 // fp8 P.V, per (b, h): the channel maxima over all Q blocks, then the E4M3
 // scale s_d = fp32(max / 448) and its inverse fp32(448 / max) (0 for an all-zero
-// channel).
-__global__ __launch_bounds__(128) void vscale_kernel(const float* vmaxp, Dims d, float* vscale,
-                                                     float* vinv) {
-  const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < d.D; c += 128) {
-    float m = 0.0f;
-    for (int i = 0; i < d.nQ; ++i) m = fmaxf(m, vmaxp[((int64_t)bh * d.nQ + i) * d.D + c]);
-    vscale[(int64_t)bh * d.D + c] = m / 448.0f;
-    vinv[(int64_t)bh * d.D + c] = m > 0.0f ? 448.0f / m : 0.0f;
+// channel).  1024 threads: thread t reduces channel t % D over the Q blocks
+// i = t / D (mod 1024 / D), eight independent loads in flight, then the
+// 1024 / D partial maxima of each channel meet in LDS.
+__global__ __launch_bounds__(1024) void vscale_kernel(const float* vmaxp, Dims d, float* vscale,
+                                                      float* vinv) {
+  __shared__ float part[1024];
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int c = t % d.D, r0 = t / d.D, rs = 1024 / d.D;
+  const float* src = vmaxp + (int64_t)bh * d.nQ * d.D + c;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = r0;
+  for (; i + 7 * rs < d.nQ; i += 8 * rs) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], src[(int64_t)(i + u * rs) * d.D]);
+  }
+  for (; i < d.nQ; i += rs) m[0] = fmaxf(m[0], src[(int64_t)i * d.D]);
+  part[t] = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+  __syncthreads();
+  if (t < d.D) {
+    float mx = 0.0f;
+    for (int r = 0; r < rs; ++r) mx = fmaxf(mx, part[r * d.D + t]);
+    vscale[(int64_t)bh * d.D + t] = mx / 448.0f;
+    vinv[(int64_t)bh * d.D + t] = mx > 0.0f ? 448.0f / mx : 0.0f;
   }
 }
 
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(256) void vt8_kernel(View v, Dims d, const float* v
 
 hipError_t launch_vt8(const View& v, int dtype, const Dims& d, const float* vmaxp, float* vscale,
                       float* vinv, unsigned char* vt, hipStream_t s) {
-  vscale_kernel<<<dim3((unsigned)(d.B * d.H)), 128, 0, s>>>(vmaxp, d, vscale, vinv);
+  vscale_kernel<<<dim3((unsigned)(d.B * d.H)), 1024, 0, s>>>(vmaxp, d, vscale, vinv);
   const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nK));
   if (dtype == kF16) {
     if (d.D == 64) vt8_kernel<kF16, 64><<<grid, 256, 0, s>>>(v, d, vinv, vt);
