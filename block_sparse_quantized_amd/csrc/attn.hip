@@ -130,6 +130,18 @@ template <int N>
 __device__ __forceinline__ void lds_wait(s16x4& a, s16x4& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
+// 16-byte LDS read (ds_read_b128) at a per-lane address plus an immediate offset,
+// issued as inline asm for the same reason as ds_read_tr; waited with lds_wait16.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16(unsigned int addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait16(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -430,31 +442,42 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   typedef std::conditional_t<QK8, i32x16, f32x16> acc_t;
 
   // Raw Q.K^T of the block staged in K stage KS (MFMAs only; no waits on results).
+  // The K fragments of k-step s sit at row krow_l (kt = 0) and row krow_l + KTROW
+  // (kt = 1, the same granule swizzle), granule (2s + hf) ^ f(row): per-lane offsets
+  // koff_s, and the kt = 1 read is the same address plus an immediate.  The reads run
+  // KSLOT - 1 k-steps ahead of the MFMAs (inline asm with explicit waits).
+  constexpr int KSTEPS = QK8 ? KS8 : KS16;
+  constexpr int KSLOT = 3;
+  unsigned int koffs[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+    koffs[s] = (unsigned int)(krow_l * KROW + 16 * ((2 * s + hf) ^ fkx<KG, PV8>(krow_l)));
   auto qk = [&](auto kstage, acc_t (&acc)[2]) {
-    const unsigned char* Kst = decltype(kstage)::value ? Ks1 : Ks0;
+    const unsigned int kb = (unsigned int)(size_t)(lds_u8_ptr)(decltype(kstage)::value ? Ks1 : Ks0);
     acc[0] = (acc_t)(0);
     acc[1] = (acc_t)(0);
-    if constexpr (!QK8) {
+    u32x4 kf[KSLOT][2];
+    auto kissue = [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const unsigned int a = kb + koffs[s];
+      kf[s % KSLOT][0] = ds_read16<0>(a);
+      kf[s % KSLOT][1] = ds_read16<KTROW * KROW>(a);
+    };
+    static_for<0, (KSLOT - 1 < KSTEPS ? KSLOT - 1 : KSTEPS)>(kissue);
+    static_for<0, KSTEPS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int ahead = (KSTEPS - 1 - s) < (KSLOT - 2) ? (KSTEPS - 1 - s) : (KSLOT - 2);
+      lds_wait16<2 * ahead>(kf[s % KSLOT][0], kf[s % KSLOT][1]);
+      if constexpr (s + KSLOT - 1 < KSTEPS) kissue(std::integral_constant<int, s + KSLOT - 1>{});
 #pragma unroll
-      for (int s = 0; s < KS16; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int rr = KTROW * kt + krow_l;
-          const int pg = (2 * s + hf) ^ fkx<KG, PV8>(rr);
-          const u16x8 kf = *(const u16x8*)(Kst + rr * KROW + 16 * pg);
-          acc[kt] = mma16<IN_F16>(kf, qf[s], acc[kt]);
-        }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS8; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int rr = KTROW * kt + krow_l;
-          const int pg = (2 * s + hf) ^ fkx<KG, PV8>(rr);
-          const i32x4 kf = *(const i32x4*)(Kst + rr * KROW + 16 * pg);
-          acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8[s], acc[kt], 0, 0, 0);
-        }
-    }
+      for (int kt = 0; kt < 2; ++kt) {
+        if constexpr (!QK8)
+          acc[kt] = mma16<IN_F16>(__builtin_bit_cast(u16x8, kf[s % KSLOT][kt]), qf[s], acc[kt]);
+        else
+          acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kf[s % KSLOT][kt]),
+                                                          q8[s], acc[kt], 0, 0, 0);
+      }
+    });
   };
 
   // Scores as fp32 with invisible keys at -inf, and the row max of the raw scores
