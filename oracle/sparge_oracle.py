@@ -505,10 +505,15 @@ def attend_head_int8_sim(q32, k32, v, mask_bh, causal, q_rows=Q_QUANT_ROWS, scal
 #   * V: one fp32 scale per (head, channel) over the whole sequence,
 #     s_d = fp32(max_n |v_nd| / 448), and codes e4m3(fp32(v_nd * fp32(448 / max)));
 #     a channel that is all zero gets scale 0 and zero codes;
-#   * P: each softmax numerator, taken as 2^(z log2(e) - ceil(row max log2(e))) (so
-#     the largest lies in (1/2, 1]), rounded to E4M3; the normaliser is the sum of
-#     the ROUNDED numerators, so the weights of a row still sum to one;
-#   * O = (sum_n e4m3(P_n) * code_nd) * s_d / sum_n e4m3(P_n), accumulated in fp64.
+#   * P, online as in flash attention: the kept blocks are visited in ascending
+#     order; before block j each row's reference M moves to ceil(running max of
+#     z log2(e)) over the blocks so far, the accumulators are rescaled by the
+#     (exact) power of two 2^(M_old - M), and the block's numerators are
+#     e4m3(2^(z log2(e) - M + 8)): the largest lies in (2^7, 2^8], near the top of
+#     the E4M3 range, so long rows keep their small weights (E4M3 spans only 2^-9
+#     to 448);
+#   * the normaliser is the sum of the ROUNDED numerators, so the weights of a row
+#     still sum to one; O = (sum P~ code) * s_d / sum P~, accumulated in fp64.
 # ---------------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -544,23 +549,26 @@ def fp8_v_quant(v32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def _pv8_group(z_blocks, c_blocks, sv, G, D):
-    """O rows of one filter group from its logit blocks and E4M3 V code blocks."""
-    if not z_blocks:
-        return np.zeros((G, D))
-    Z = np.concatenate(z_blocks, axis=1)
-    C = np.concatenate(c_blocks, axis=0)
-    # P = 2^(z log2(e) - M) with M = ceil(row max * log2(e)): the row max lands in
-    # (1/2, 1], and any other integer M' >= M only multiplies every P by a power of
-    # two, which E4M3 rounding commutes with outside its subnormal range
-    m = Z.max(axis=1) * LOG2E
-    ok = np.isfinite(m)
-    M = np.where(ok, np.ceil(m), 0.0)
-    Pr = e4m3_round(np.exp2(Z * LOG2E - M[:, None]))
-    l = Pr.sum(axis=1)
-    o = (Pr @ C) * sv.astype(np.float64)[None, :]
+    """O rows of one filter group from its logit blocks (in visiting order) and their
+    E4M3 V code blocks, with the online integer reference of the fp8 reading."""
+    O = np.zeros((G, D))
+    l = np.zeros(G)
+    M = np.full(G, -np.inf)
+    for z, C in zip(z_blocks, c_blocks):
+        x = z * LOG2E
+        mloc = x.max(axis=1)
+        M_new = np.where(np.isfinite(mloc), np.maximum(M, np.ceil(mloc)), M)
+        f = np.where(np.isfinite(M), np.exp2(np.where(np.isfinite(M), M - M_new, 0.0)), 1.0)
+        O *= f[:, None]
+        l *= f
+        M = M_new
+        ok = np.isfinite(M)
+        P = e4m3_round(np.exp2(x - np.where(ok, M, 0.0)[:, None] + 8.0) * ok[:, None])
+        O += P @ C
+        l += P.sum(axis=1)
     out = np.zeros((G, D))
     nz = l > 0
-    out[nz] = o[nz] / l[nz, None]
+    out[nz] = O[nz] * sv.astype(np.float64)[None, :] / l[nz, None]
     return out
 
 
@@ -571,8 +579,8 @@ def attend_rows_pv8(q, k, v, mask_bh, groups, causal, scale=None, lam=None, grou
     V: per-channel E4M3 codes over the whole head (``fp8_v_quant``).  Logits: the
     exact fp64 ones (qk="exact") or the int8 ones of ``attend_head_int8_sim``
     (qk="int8").  The filter, when ``lam`` is set, runs on those logits as in
-    ``attend_group``.  Then P = 2^(z log2(e) - ceil(row max log2(e))) over the
-    remaining keys, rounded to E4M3, and O = (sum P~ code) * s / sum P~ in fp64.
+    ``attend_group``.  The remaining blocks then enter ``_pv8_group`` in visiting
+    order (online integer reference, numerators at 2^8 scale, rounded to E4M3).
     Returns O rows in fp64."""
     q32 = np.asarray(q, dtype=np.float32)
     k32 = np.asarray(k, dtype=np.float32)
