@@ -620,10 +620,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       }
     }
     if (!skip) {
-      if (__ballot(mx > m_ref + kTau) != 0ull) {
-        // fp8 P.V: the reference max is rounded up to an integer, so that every
-        // rescale is by a power of two and E4M3 rounds P exactly as it would round
-        // 2^(x - ceil(row max)) times that power (outside the subnormal range)
+      // fp8 P.V: the reference is the integer ceiling of the row's running max, moved
+      // as soon as the max passes it (no slack): every P of the block is then
+      // 2^(x - reference + 8) <= 2^8, inside E4M3's range with its largest values
+      // near the top of it, and every rescale is an exact power of two
+      if (__ballot(mx > m_ref + (PV8 ? 0.0f : kTau)) != 0ull) {
         const float m_ref_new = PV8 ? __builtin_ceilf(fmaxf(m_ref, mx)) : fmaxf(m_ref, mx);
         const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
         const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
@@ -642,10 +643,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int q = 0; q < 2; ++q) vfr[dt][q] = *(const u32x4*)(Vst + v8a[q] + 2048 * dt);
-        // P = 2^(score * slope + offset - m_use) as E4M3: word q holds keys
+        // P = 2^(score * slope + offset - m_use + 8) as E4M3: word q holds keys
         // 32hf + 4q .. +3, which are sc_cur[q / 4][4(q % 4) .. +3]
         const float slope = QK8 ? slope_i8 : p.c;
-        const float offs = (QK8 ? bias : 0.0f) - m_use;
+        const float offs = (QK8 ? bias : 0.0f) - m_use + 8.0f;
         i32x8 pb;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {

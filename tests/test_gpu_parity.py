@@ -545,6 +545,58 @@ def sample_groups(B, H, N, n, seed, causal, ok=None):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,variant", [("llm128k", "fp8"), ("llm8k", "cdf"), ("llm128k", "cdf")])
+def test_full_workload_variant(dev, name, variant):
+    """The bench's extra paths at full size: int8 Q.K^T with fp8 P.V, and the
+    threshold selection (mass 0.95) -- the whole mask, sampled outputs."""
+    wl = synth.WORKLOADS[name]
+    say(f"full workload {name} ({variant}): generating on {dev}")
+    q, k, v = synth.make_qkv(wl, device=dev)
+    lam = -10.0 if wl.filter_on else None
+    if variant == "fp8":
+        out, gm, st = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
+                                           qk_int8=True, pv_fp8=True, return_mask=True, stats=True)
+        params = so.OracleParams(topk=wl.topk, causal=wl.causal)
+    else:
+        out, gm, st = bsq.sparge_cdf_attn(q, k, v, 0.95, wl.causal, filter_on=wl.filter_on,
+                                          qk_int8=wl.qk_int8, pv_fp16=wl.pv_fp16, return_mask=True,
+                                          stats=True)
+        params = so.OracleParams(cdf=0.95, causal=wl.causal)
+    torch.cuda.synchronize()
+    g = gm.cpu().numpy().astype(bool)
+    om, infos = oracle_predict(q, k, params)
+    if variant == "fp8":
+        bad, exc = unexcused_mismatches(g, om, infos)
+    else:
+        bad, exc = cdf_mismatches(g, om, infos, 0.95), None
+    same = (g == om).all(axis=3)
+    say(f"  mask: unexcused {bad}, excused {exc}, rows differing {int((~same).sum())}, "
+        f"density {om.mean():.3f}, stats {st}")
+    assert bad == 0
+    assert st["kept_blocks"] == int(g.sum())
+    B, H, N, D = q.shape
+    worst = 0.0
+    heads = {}
+    for (b, h, i, gi) in sample_groups(B, H, N, 8, seed=len(name) + 7, causal=wl.causal, ok=same):
+        if (b, h) not in heads:
+            heads[(b, h)] = (f64(q[b, h]), f64(k[b, h]), f64(v[b, h]))
+        qn, kn, vn = heads[(b, h)]
+        if variant == "fp8":
+            ref = so.attend_rows_pv8(qn, kn, vn, om[b, h], [(i, gi)], wl.causal, lam=lam,
+                                     qk="int8")[(i, gi)]
+            tol = TOLF8 * max(1.0, np.abs(vn).max() / 4)
+        else:
+            ref = so.attend_rows(qn, kn, vn, om[b, h], [(i, gi)], wl.causal, lam=lam)[(i, gi)]
+            tol = TOL8 if wl.qk_int8 else TOL16
+        t0 = 128 * i + 32 * gi
+        got = f64(out[b, h, t0:t0 + ref.shape[0]])
+        err = np.abs(got - ref).max()
+        worst = max(worst, err / tol)
+        say(f"  sample b={b} h={h} i={i} g={gi}: err {err:.3e} (tol {tol:.1e})")
+    assert worst < 1.0
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["llm8k", "image", "video", "llm128k"])
 def test_full_workload(dev, name):
     wl = synth.WORKLOADS[name]
