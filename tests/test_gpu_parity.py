@@ -366,6 +366,28 @@ def test_fp8_pv_topk(dev, N, D, causal, qk8):
     assert err < TOLF8 * max(1.0, vmax / 4)
 
 
+@pytest.mark.parametrize("path", ["fp8_int8", "fp8_bf16", "cdf", "cdf_fp8_int8"])
+def test_strided_inputs_match_contiguous(dev, path):
+    # (B, N, H, D) storage viewed as (B, H, N, D): every kernel that reads Q, K or V
+    # (preparation, V scales and E4M3 tiles, attention) must give bit-identical
+    # results to the contiguous copies
+    B, H, N, D = 2, 3, 777, 128
+    g = torch.Generator(device="cpu").manual_seed(31)
+    base = [(torch.randn((B, N, H, D), generator=g)).to(torch.bfloat16).to(dev) for _ in range(3)]
+    qs, ks, vs = (t.transpose(1, 2) for t in base)
+    qc, kc, vc = (t.contiguous() for t in (qs, ks, vs))
+    assert not qs.is_contiguous()
+    kw = dict(qk_int8=path.endswith("int8"), pv_fp8="fp8" in path, return_mask=True)
+    fn = (lambda *a, **k: bsq.sparge_cdf_attn(*a, 0.9, True, **k)) if path.startswith("cdf") else \
+         (lambda *a, **k: bsq.sparge_topk_attn(*a, 0.5, True, **k))
+    o1, m1 = fn(qs, ks, vs, **kw)
+    o2, m2 = fn(qc, kc, vc, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(m1, m2)
+    assert torch.equal(o1, o2)
+    say(f"strided == contiguous for {path}: density {m1.float().mean().item():.3f}")
+
+
 def test_fp8_pv_fp32_inputs_unsupported(dev):
     q, k, v = rand_qkv(1, 1, 256, 64, torch.float32, dev, seed=1)
     with pytest.raises(Exception):
