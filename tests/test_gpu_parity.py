@@ -567,6 +567,44 @@ def sample_groups(B, H, N, n, seed, causal, ok=None):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("cdf", [None, 0.9])
+def test_max_sequence_length(dev, cdf):
+    """N = 262144, the largest the ABI accepts: 4096 K blocks per row fill the
+    selector's per-thread key slots and the uint16 block lists."""
+    wl = synth.workload("llm8k", H=1, N=262144, D=64, seed=9)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    if cdf is None:
+        out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, True, return_mask=True)
+        params = so.OracleParams(topk=0.5, causal=True)
+    else:
+        out, gm = bsq.sparge_cdf_attn(q, k, v, cdf, True, return_mask=True)
+        params = so.OracleParams(cdf=cdf, causal=True)
+    torch.cuda.synchronize()
+    g = gm.cpu().numpy().astype(bool)
+    om, infos = oracle_predict(q, k, params)
+    bad = unexcused_mismatches(g, om, infos)[0] if cdf is None else cdf_mismatches(g, om, infos, cdf)
+    same = (g == om).all(axis=3)
+    say(f"N=262144 cdf={cdf}: unexcused {bad}, rows differing {int((~same).sum())}, "
+        f"density {om.mean():.3f}, longest row {int(om.sum(axis=3).max())} blocks")
+    assert bad == 0
+    qn, kn, vn = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
+    # the random-walk generator drifts further at this length (max |v| about 14 here,
+    # against 4-5 at 8K), so |O| reaches 10 and the bf16 output alone rounds by up to
+    # half an ulp, 2^-5 = 0.031: the bar is the 16-bit tolerance scaled by max|v| / 4,
+    # as for the fp8 path
+    tol = TOL16 * max(1.0, np.abs(vn).max() / 4)
+    worst = 0.0
+    for (b, h, i, gi) in sample_groups(1, 1, wl.N, 6, seed=11, causal=True, ok=same):
+        ref = so.attend_rows(qn, kn, vn, om[0, 0], [(i, gi)], True, lam=-10.0)[(i, gi)]
+        t0 = 128 * i + 32 * gi
+        err = np.abs(f64(out[0, 0, t0:t0 + ref.shape[0]]) - ref).max()
+        worst = max(worst, err)
+        say(f"  sample i={i} g={gi}: err {err:.3e}, max|ref| {np.abs(ref).max():.2f}")
+    say(f"  max|v| {np.abs(vn).max():.2f}, tolerance {tol:.3e}")
+    assert worst < tol
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,variant", [("llm128k", "fp8"), ("llm8k", "cdf"), ("llm128k", "cdf")])
 def test_full_workload_variant(dev, name, variant):
     """The bench's extra paths at full size: int8 Q.K^T with fp8 P.V, and the
