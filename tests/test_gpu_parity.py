@@ -210,6 +210,26 @@ def test_tiny_workload_end_to_end(dev):
     assert err < TOL16
 
 
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_topk_attn_small_shapes(dev, N, D, causal):
+    """The whole call on ragged and boundary lengths: mask bit-exact, output within the
+    16-bit bar (block-correlated inputs, so that the similarity gate and the top-k
+    selection are both live)."""
+    wl = synth.workload("tiny", H=2, N=N, D=D, dtype=torch.bfloat16)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, causal, return_mask=True)
+    torch.cuda.synchronize()
+    om, infos = oracle_predict(q, k, so.OracleParams(topk=0.5, causal=causal))
+    bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+    assert bad == 0 and exc == 0
+    ref, _ = oracle_outputs(q, k, v, om, causal, lam=-10.0)
+    err = np.abs(f64(out) - ref).max()
+    say(f"small shape N={N} D={D} causal={causal}: density {om.mean():.3f}, err {err:.3e}")
+    assert err < TOL16
+
+
 @pytest.mark.parametrize("N,D,causal", [(700, 64, True), (1000, 128, False), (129, 128, True)])
 def test_topk_attn_topk1_filter_off_is_dense(dev, N, D, causal):
     q, k, v = rand_qkv(1, 2, N, D, torch.bfloat16, dev, seed=N)
