@@ -140,6 +140,35 @@ class Path:
         return r
 
 
+def graph_replay(path, steps):
+    """The same step captured once in a HIP graph (the library allocates nothing and
+    does not synchronise without stats) and replayed: per-step time without the
+    host-side launch gaps, or None when capture is unavailable."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            path.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            path.step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    except Exception as e:  # capture not supported by this runtime / build
+        log(f"[bench] graph replay unavailable: {e}")
+        return None
+
+
 def time_path(path, ev, steps, warmup):
     """Whole-step wall time (synchronised) and per-launch attention-kernel time."""
     import torch
@@ -379,6 +408,10 @@ def main():
 
     extras = {}
     if not args.no_extras:
+        gr = graph_replay(path, args.steps)
+        if gr is not None:
+            extras["graph_replay"] = {"ms_per_step": round(gr, 4),
+                                      "tops_dense_equiv": round(dense / (gr * 1e-3) / 1e12, 2)}
         if path.qk_int8 or path.pv_fp16:
             p16 = Path(wl, dev, qk_int8=False, pv_fp16=False,
                        inputs=(path.q, path.k, path.v, path.mask))

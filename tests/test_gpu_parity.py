@@ -408,6 +408,36 @@ def test_strided_inputs_match_contiguous(dev, path):
     say(f"strided == contiguous for {path}: density {m1.float().mean().item():.3f}")
 
 
+@pytest.mark.parametrize("pv_fp8", [False, True])
+def test_graph_replay_matches_eager(dev, pv_fp8):
+    """The library's launches captured in a HIP graph (no allocation, no host sync, no
+    memset in the call): every replay, with eager work and synchronisations between
+    the replays, reproduces the eager result bit for bit."""
+    wl = synth.workload("llm8k", H=4, N=3000, D=128)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    ws = torch.empty(bsq.sparge_workspace_bytes(*q.shape, q.dtype), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    kw = dict(qk_int8=True, pv_fp16=not pv_fp8, pv_fp8=pv_fp8, out=out, workspace=ws)
+    eager = bsq.sparge_topk_attn(q, k, v, 0.5, True, **kw).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        bsq.sparge_topk_attn(q, k, v, 0.5, True, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bsq.sparge_topk_attn(q, k, v, 0.5, True, **kw)
+    for rep in range(3):
+        out.fill_(float("nan"))            # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager result"
+    say(f"graph replay == eager (pv_fp8={pv_fp8}) over 3 replays")
+
+
 def test_fp8_pv_fp32_inputs_unsupported(dev):
     q, k, v = rand_qkv(1, 1, 256, 64, torch.float32, dev, seed=1)
     with pytest.raises(Exception):
