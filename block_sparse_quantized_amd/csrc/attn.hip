@@ -679,23 +679,26 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         };
         static_for<0, kVAhead>(issue);
         __builtin_amdgcn_sched_barrier(0);   // keep these reads ahead of the exponentials
-        // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs
+        // P = 2^(score * slope + offset - m_use), rounded to the P.V type in pairs.  The
+        // B fragment of k-step k (pw[k]) holds keys 32(k/2) + 16(k%2) + ..; each is made
+        // just before it is needed, so the exponentials of k-step k+1 run under the
+        // MFMAs of k-step k.
         const float slope = QK8 ? slope_i8 : p.c;
         const float offs = (QK8 ? bias : 0.0f) - m_use;
         u32x4 pw[4];
+        auto make_pw = [&](auto kc) {
+          constexpr int k = decltype(kc)::value, kt = k >> 1, sg = k & 1;
   #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-  #pragma unroll
-          for (int sg = 0; sg < 2; ++sg)
-  #pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-              const int r = 8 * sg + 2 * wd;
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
-              const unsigned int pr = pack2<PV_F16>(p0, p1);
-              l_acc = add_pair<PV_F16>(pr, l_acc);
-              pw[2 * kt + sg][wd] = pr;
-            }
+          for (int wd = 0; wd < 4; ++wd) {
+            const int r = 8 * sg + 2 * wd;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
+            const unsigned int pr = pack2<PV_F16>(p0, p1);
+            l_acc = add_pair<PV_F16>(pr, l_acc);
+            pw[k][wd] = pr;
+          }
+        };
+        make_pw(std::integral_constant<int, 0>{});
         static_for<0, kNU>([&](auto uc) {
           constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
           if constexpr (u + kVAhead < kNU) issue(std::integral_constant<int, u + kVAhead>{});
@@ -705,6 +708,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           lds_wait<2 * later>(f0, f1);
           const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
+          if constexpr (dt == 0 && sg + 1 < 4) make_pw(std::integral_constant<int, sg + 1>{});
         });
       }
       }
