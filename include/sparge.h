@@ -158,7 +158,7 @@ sparge_status sparge_cdf_attn(const sparge_tensor* q, const sparge_tensor* k,
  * nonzero keeps the 128x64 block; NULL keeps every block.  Not causal (the call
  * has no is_causal argument).  A query row with no kept block outputs zeros.
  * opts->head_filter_lambda applies; head_select and head_sim_threshold are
- * ignored. */
+ * validated but not used. */
 sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
                                 const sparge_tensor* v, const uint8_t* mask_id,
                                 const sparge_tensor* out, const sparge_opts* opts,
@@ -167,7 +167,7 @@ sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,
 /* Stage 1 only: writes the predicted block mask to mask_out (device uint8,
  * (B, H, ceil(N/128), ceil(N/64)), contiguous).  Same arguments and rules as
  * sparge_topk_attn; opts->mask_out is ignored.  With opts->head_select the topk
- * argument is replaced per head; head_filter_lambda is ignored. */
+ * argument is replaced per head; head_filter_lambda is validated but not used. */
 sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k, double topk,
                                   int32_t is_causal, const sparge_opts* opts, uint8_t* mask_out,
                                   void* workspace, size_t workspace_bytes, void* stream);
