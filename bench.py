@@ -243,17 +243,12 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
     import numpy as np
 
     from oracle import sparge_oracle as so
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = int(blas[0]["num_threads"]) if blas else 1
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
     B, H, N, D = q.shape
     qn = q[0, 0].double().cpu().numpy()
     kn = k[0, 0].double().cpu().numpy()
     vn = v[0, 0].double().cpu().numpy()
     t0 = time.perf_counter()
+    c0 = time.process_time()   # CPU time of every thread of this process
     if wl.api == "block_sparse":
         from block_sparse_quantized_amd import synth
         mask = synth.make_block_mask(wl, device="cpu")[0, 0].numpy().astype(bool)
@@ -286,6 +281,9 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
             done_rows += r1 - r0
             groups.append((i, g))
     t = t_attn + t_pred * done_rows / N
+    # cores actually used: CPU time over wall time of the sampled run (the oracle's
+    # small matrix products leave most of the BLAS threads idle)
+    cores = round((time.process_time() - c0) / max(1e-9, time.perf_counter() - t0), 1)
     return {"value": round(dense_ops / t / 1e12, 8), "unit": "TOPS (dense-equivalent)",
             "cores": cores, "kind": "oracle",
             "sample": (f"head (0,0) of {wl.name}: full stage-1 oracle predictor ({t_pred:.2f}s, "
@@ -293,7 +291,9 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
                        f"{' with the filter' if lam is not None else ''} for {len(groups)} "
                        f"32-row groups ({done_rows} rows in {len(set(i for i, _ in groups))} block rows, "
                        f"spread over the sequence, longest first); "
-                       f"value = dense-equivalent ops of those rows / time ({t:.2f}s)")}
+                       f"value = dense-equivalent ops of those rows / time ({t:.2f}s); cores = CPU "
+                       f"time / wall time of the run, on a host with {len(os.sched_getaffinity(0))} "
+                       f"usable cores")}
 
 
 def sdpa_baseline(q, k, v, causal, steps=3):
