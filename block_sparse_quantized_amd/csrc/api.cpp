@@ -18,9 +18,9 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   const size_t BH = (size_t)d.B * d.H;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
-  w.qmean = take(BH * d.nQ * d.D * sizeof(double));
+  w.qmean = take(BH * pad16(d.nQ) * d.D * sizeof(double));
   w.qsim = take(BH * d.nQ * sizeof(double));
-  w.kmean = take(BH * d.nK * d.D * sizeof(double));
+  w.kmean = take(BH * pad16(d.nK) * d.D * sizeof(double));
   w.ksim = take(BH * d.nK * sizeof(double));
   w.scores = take(BH * d.nQ * d.nK * sizeof(double));
   w.lists = take(BH * d.nQ * d.lstride * sizeof(uint16_t));

@@ -121,70 +121,94 @@ __global__ __launch_bounds__(256) void block_stats_kernel(View q, View k, Dims d
   }
   double* means = isq ? qmean : kmean;
   const int nb = isq ? d.nQ : d.nK;
-  double* out = means + ((int64_t)bh * nb + blk) * D;
   double sq = 0.0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    out[CPL * lane + c] = s[c] / (double)n;
+    means[mean_index(bh, pad16(nb), blk, CPL * lane + c, D)] = s[c] / (double)n;
     sq = sq + u[c] * u[c];
   }
   sq = wave_sum_f64(sq);
   if (lane == 0) (isq ? qsim : ksim)[(int64_t)bh * nb + blk] = sq / (double)(n * n);
 }
 
-// Pooled scores, one 64 (i) x 64 (j) tile per workgroup of 256 threads, 4 x 4
-// scores per thread; the block means stage through LDS channel-major in 32-channel
-// chunks.  Each score is one fused multiply-add chain in channel order.  Tiles
-// holding no valid pair under causality are skipped.
+// Pooled scores on the fp64 matrix cores (v_mfma_f64_16x16x4_f64): one 64 (i) x
+// 64 (j) tile per workgroup, a 32 x 32 quarter per wavefront as 2 x 2 MFMA tiles.
+// In the MFMA's operand layout lane (r, kq) = (lane % 16, lane / 16) supplies row
+// r of a 16-row tile at k = kq; at k-step s that is channel (D/4) kq + s, the same
+// channel for the Q and the K operand.  The means are stored in that order
+// (mean_index), so each 16-byte load of a wavefront (two k-steps of one 16-row
+// tile) is 1 KB of contiguous memory.  Every pair sums all D products in fp64;
+// only the association differs from a plain dot product.  Tiles and quarters
+// holding no valid pair under causality are skipped; tiles past the padded ends
+// re-read the last tile and rows and columns past the ends are not stored.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qmean, const double* kmean,
                                                             Dims d, int causal, double scale,
                                                             double* scores) {
-  constexpr int DC = 32;
-  __shared__ double qm[DC][64 + 1];
-  __shared__ double km[DC][64 + 1];
+  constexpr int NP = D / 8;    // k-step pairs
+  constexpr int CP = 4;        // pairs per chunk
   const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
   if (causal && j0 > 2 * (i0 + 63) + 1) return;
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tj = tid & 15;   // rows i0 + ti + 16a, columns j0 + tj + 16b
-  double acc[4][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int iw = i0 + 32 * (w >> 1), jw = j0 + 32 * (w & 1);
+  // no barriers below, so a wavefront with no valid pair may leave early
+  if (causal && jw > 2 * (iw + 31) + 1) return;
+  const int nQp = pad16(d.nQ), nKp = pad16(d.nK);
+  const double2* qa[2];
+  const double2* kb[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
-  for (int c0 = 0; c0 < D; c0 += DC) {
-#pragma unroll
-    for (int e0 = 0; e0 < 64 * DC; e0 += 256) {
-      const int e = e0 + tid, r = e / DC, cc = e % DC;
-      const int i = i0 + r, j = j0 + r;
-      qm[cc][r] = i < d.nQ ? qmean[((int64_t)bh * d.nQ + i) * D + c0 + cc] : 0.0;
-      km[cc][r] = j < d.nK ? kmean[((int64_t)bh * d.nK + j) * D + c0 + cc] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int cc = 0; cc < DC; ++cc) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = qm[cc][ti + 16 * a];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = km[cc][tj + 16 * c];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
-    }
-    __syncthreads();
+  for (int t = 0; t < 2; ++t) {
+    qa[t] = (const double2*)(qmean + ((int64_t)bh * nQp + min(iw + 16 * t, nQp - 16)) * D) + lane;
+    kb[t] = (const double2*)(kmean + ((int64_t)bh * nKp + min(jw + 16 * t, nKp - 16)) * D) + lane;
   }
+  double2 a[2][2][CP], b[2][2][CP];   // [buffer][tile][pair]
+  auto load = [&](int buf, int p0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ti + 16 * a;
-    if (i >= d.nQ) continue;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tj + 16 * c;
-      if (j < d.nK) scores[((int64_t)bh * d.nQ + i) * d.nK + j] = scale * acc[a][c];
-    }
+      for (int e = 0; e < CP; ++e) {
+        a[buf][t][e] = qa[t][64 * (p0 + e)];
+        b[buf][t][e] = kb[t][64 * (p0 + e)];
+      }
+  };
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = (f64x4)(0.0);
+  load(0, 0);
+#pragma unroll
+  for (int c = 0; c < NP / CP; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < NP / CP) load(cur ^ 1, (c + 1) * CP);
+#pragma unroll
+    for (int e = 0; e < CP; ++e)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int tj = 0; tj < 2; ++tj) {
+            const double av = half ? a[cur][ti][e].y : a[cur][ti][e].x;
+            const double bv = half ? b[cur][tj][e].y : b[cur][tj][e].x;
+            acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti][tj], 0, 0, 0);
+          }
   }
+  // lane (r, kq) holds rows kq + 4e (e = 0..3) of column r of each output tile
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+      const int j = jw + 16 * tj + r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = iw + 16 * ti + kq + 4 * e;
+        if (i < d.nQ && j < d.nK) scores[((int64_t)bh * d.nQ + i) * d.nK + j] = scale * acc[ti][tj][e];
+      }
+    }
 }
 
 // Order-preserving map of an fp64 score to uint64 (larger score -> larger key);
@@ -203,14 +227,251 @@ __device__ __forceinline__ int keep_count(int C, double topk) {
   return kk > C ? C : kk;
 }
 
-// One workgroup of 256 threads per block row (b, h, i).  Thread t holds the keys
-// of blocks j = t + 256m in registers (all loads issued up front).  The k-th
-// largest candidate key is found exactly by a radix select over 8-bit digits from
-// the most significant (an LDS histogram per pass over the keys that still match
-// the prefix, a suffix scan by one wavefront), stopping early once a single key
-// matches.  Ties at the threshold go to the lowest block indices; the kept blocks
-// are written in ascending order (ballots, then a prefix over the four waves).
-constexpr int kSelMaxM = 16;  // keys per thread: nK <= 4096
+// Wave-level reductions and scans on DPP lane moves and the gfx950 row swaps (no
+// LDS round trips).  A butterfly inside each 16-lane row (partner lane^1 and lane^2
+// by quad permutes, then the mirrored lane of the 8-lane half and of the row), then
+// across rows (v_permlane16_swap: rows 0<->1 and 2<->3; v_permlane32_swap: the two
+// halves); every lane receives the result.
+template <int CTRL>
+__device__ __forceinline__ unsigned int dpp_u32(unsigned int v) {
+  return (unsigned int)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
+}
+// the value of the partner lane in the row (S = 16) or half (S = 32) swap
+template <int S>
+__device__ __forceinline__ unsigned int swap_partner(unsigned int v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((lane >> 4) & 1) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane >> 5) ? r[0] : r[1];
+  }
+}
+template <class F>
+__device__ __forceinline__ unsigned int wave_allreduce_u32(unsigned int v, F op) {
+  v = op(v, dpp_u32<0xb1>(v));     // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_u32<0x4e>(v));     // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_u32<0x141>(v));    // row_half_mirror
+  v = op(v, dpp_u32<0x140>(v));    // row_mirror
+  v = op(v, swap_partner<16>(v));
+  v = op(v, swap_partner<32>(v));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return (int)wave_allreduce_u32((unsigned int)v, [](unsigned int x, unsigned int y) { return x + y; });
+}
+template <class F>
+__device__ __forceinline__ unsigned long long wave_allreduce_u64(unsigned long long v, F pick) {
+  auto step = [&](unsigned int lo, unsigned int hi) {
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    v = pick(v, o);
+  };
+#define SPARGE_STEP(EXPR_LO, EXPR_HI) step(EXPR_LO, EXPR_HI)
+  SPARGE_STEP(dpp_u32<0xb1>((unsigned int)v), dpp_u32<0xb1>((unsigned int)(v >> 32)));
+  SPARGE_STEP(dpp_u32<0x4e>((unsigned int)v), dpp_u32<0x4e>((unsigned int)(v >> 32)));
+  SPARGE_STEP(dpp_u32<0x141>((unsigned int)v), dpp_u32<0x141>((unsigned int)(v >> 32)));
+  SPARGE_STEP(dpp_u32<0x140>((unsigned int)v), dpp_u32<0x140>((unsigned int)(v >> 32)));
+  SPARGE_STEP(swap_partner<16>((unsigned int)v), swap_partner<16>((unsigned int)(v >> 32)));
+  SPARGE_STEP(swap_partner<32>((unsigned int)v), swap_partner<32>((unsigned int)(v >> 32)));
+#undef SPARGE_STEP
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  return wave_allreduce_u64(v, [](unsigned long long x, unsigned long long y) { return y > x ? y : x; });
+}
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+  return wave_allreduce_u64(v, [](unsigned long long x, unsigned long long y) { return y < x ? y : x; });
+}
+// Inclusive prefix sum over the lanes in lane order: shifts by 1, 2, 4 and 8 inside
+// each row (lanes without a source add 0), then the last lane of row 0 (and of row
+// 2) added to row 1 (row 3), then lane 31 added to rows 2 and 3.
+__device__ __forceinline__ unsigned int wave_incl_scan_u32(unsigned int v) {
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+// Top-k selection, one wavefront per block row (b, h, i), four rows per workgroup
+// and no workgroup barriers.  Lane l holds the keys of blocks j = l + 64m (m < MK,
+// nK <= 64 MK), so every chunk m is 64 consecutive blocks in lane order.  The
+// k-th largest candidate key is located exactly by a radix select over 8-bit
+// digits: the leading bits shared by every candidate (from the wave's smallest and
+// largest key) are skipped, then each pass histograms the keys that match the
+// prefix found so far in the wavefront's own LDS bins and walks the bins from the
+// largest digit, stopping as soon as a single key matches.  Rows whose Q block is
+// not similar keep every valid block, so they skip the search.  Ties at the
+// threshold go to the lowest block indices; kept blocks are written in ascending
+// order (one ballot per chunk).
+template <int MK>
+__global__ __launch_bounds__(256) void select_topk_kernel(const double* scores, const double* qsim,
+                                                          const double* ksim, Dims d, int causal,
+                                                          SelectParams sp, uint8_t* mask_out,
+                                                          uint16_t* lists, int* counts,
+                                                          unsigned long long* counters) {
+  __shared__ __attribute__((aligned(16))) unsigned int hist_s[4][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  // no workgroup barriers in this kernel, so a wavefront past the end may leave
+  if (row >= (int64_t)d.B * d.H * d.nQ) return;
+  unsigned int* hist = hist_s[wv];
+  const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
+  const int h = bh % d.H;
+  const double theta = sp.head_theta ? sp.head_theta[h] : sp.theta;
+  const double sel = sp.head_sel ? sp.head_sel[h] : sp.sel;
+  const int nK = d.nK;
+  const int jv = causal ? min(nK, 2 * i + 2) : nK;
+  const bool simq = qsim[row] >= theta;
+  const double* srow = scores + row * nK;
+  const double* ks = ksim + (int64_t)bh * nK;
+
+  // similarity of the K blocks, then the scores of the valid ones.  The loads are
+  // unconditional, with indices clamped into the row (lanes past the end re-read its
+  // last entry), and all of a kind are in flight before the first is used.  Per-lane
+  // bit masks over m record which blocks are in the row (inm), valid (validm),
+  // similar (simkm) and candidates (candm).
+  unsigned long long inm = 0ull, validm = 0ull, simkm = 0ull, candm = 0ull;
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    inm |= (unsigned long long)(lane + 64 * m < nK) << m;
+    validm |= (unsigned long long)(lane + 64 * m < jv) << m;
+  }
+  {
+    double kv[MK];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) kv[m] = ks[min(lane + 64 * m, nK - 1)];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) asm volatile("" : "+v"(kv[m]));
+#pragma unroll
+    for (int m = 0; m < MK; ++m) simkm |= (unsigned long long)(kv[m] >= theta) << m;
+    simkm &= inm;
+  }
+  candm = validm & simkm;
+  __builtin_amdgcn_sched_barrier(0);   // the score loads reuse the registers of these
+  unsigned long long key[MK];
+  {
+    double sv[MK];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) sv[m] = srow[min(lane + 64 * m, jv - 1)];
+#pragma unroll
+    for (int m = 0; m < MK; ++m) asm volatile("" : "+v"(sv[m]));
+#pragma unroll
+    for (int m = 0; m < MK; ++m) key[m] = order_key(sv[m]) & (0ull - ((candm >> m) & 1ull));
+  }
+  const int C = wave_sum_i32(__popcll(candm));
+  const int kk = keep_count(C, sel);
+
+  unsigned long long T = 0ull;
+  int need = 0;
+  if (simq && kk > 0) {
+    unsigned long long kmax = 0ull, kmin = ~0ull;
+#pragma unroll
+    for (int m = 0; m < MK; ++m)
+      if (64 * m < jv && ((candm >> m) & 1ull)) {
+        kmax = key[m] > kmax ? key[m] : kmax;
+        kmin = key[m] < kmin ? key[m] : kmin;
+      }
+    kmax = wave_max_u64(kmax);
+    kmin = wave_min_u64(kmin);
+    int krem = kk;   // rank still to be located among the keys matching the prefix
+    if (kmax == kmin) {
+      T = kmax;      // every candidate has the same key
+    } else {
+      // bytes above the highest differing bit are common to all candidates
+      const int top = (63 - __clzll((long long)(kmax ^ kmin))) >> 3;
+      unsigned long long pmask = top == 7 ? 0ull : (~0ull << (8 * (top + 1)));
+      T = kmax & pmask;
+      for (int byte = top; byte >= 0; --byte) {
+        const int shift = 8 * byte;
+        *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int m = 0; m < MK; ++m)
+          if (64 * m < jv && ((candm >> m) & 1ull) && (key[m] & pmask) == T)
+            atomicAdd(&hist[(unsigned int)(key[m] >> shift) & 255u], 1u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l owns digits 255-4l .. 252-4l (descending); counts above it by a scan
+        const uint4 cv = *(const uint4*)(hist + 252 - 4 * lane);
+        const unsigned int c[4] = {cv.w, cv.z, cv.y, cv.x};
+        const unsigned int tot = c[0] + c[1] + c[2] + c[3];
+        unsigned int run = wave_incl_scan_u32(tot) - tot;
+        int found = -1;
+        unsigned int above = 0u, here = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (found < 0 && run + c[e] >= (unsigned int)krem) {
+            found = 255 - (4 * lane + e);
+            above = run;
+            here = c[e];
+          }
+          run += c[e];
+        }
+        const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(found >= 0)) - 1);
+        const int digit = __builtin_amdgcn_readlane(found, src);
+        krem -= __builtin_amdgcn_readlane((int)above, src);
+        const unsigned int nhere = (unsigned int)__builtin_amdgcn_readlane((int)here, src);
+        // every lane has finished reading the bins before the next pass clears them
+        __builtin_amdgcn_wave_barrier();
+        T |= (unsigned long long)digit << shift;
+        pmask |= 255ull << shift;
+        if (nhere == 1u && byte > 0) {
+          // a single key matches the prefix: it is the threshold
+          unsigned long long mine = 0ull;
+#pragma unroll
+          for (int m = 0; m < MK; ++m)
+            if (64 * m < jv && ((candm >> m) & 1ull) && (key[m] & pmask) == T) mine = key[m];
+          T = wave_max_u64(mine);
+          break;
+        }
+      }
+    }
+    need = krem;   // keys equal to T still to take, lowest block index first
+  }
+
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_before = 0, base = 0;
+  uint8_t* mrow = mask_out ? mask_out + row * nK : nullptr;
+  uint16_t* lrow = lists + row * d.lstride;
+  const bool selecting = simq && kk > 0;
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    if (64 * m >= jv) {
+      // no valid block in this chunk (causal rows): only the mask needs writing
+      if (mrow && 64 * m < nK && ((inm >> m) & 1ull)) mrow[lane + 64 * m] = 0;
+    } else {
+      const int j = lane + 64 * m;
+      const bool valid = (validm >> m) & 1ull, simk = (simkm >> m) & 1ull;
+      const bool cand = (candm >> m) & 1ull;
+      const bool is_eq = selecting && cand && key[m] == T;
+      const unsigned long long eqm = __ballot(is_eq);
+      const bool gt = selecting && cand && key[m] > T;
+      const int rank = eq_before + __popcll(eqm & lt_mask);
+      const bool keep = (valid && (!simq || !simk || gt)) || (is_eq && rank < need);
+      if (mrow && ((inm >> m) & 1ull)) mrow[j] = keep ? 1 : 0;
+      const unsigned long long km = __ballot(keep);
+      if (keep) lrow[base + __popcll(km & lt_mask)] = (uint16_t)j;
+      base += __popcll(km);
+      eq_before += __popcll(eqm);
+    }
+  }
+  if (lane == 0) {
+    counts[row] = base;
+    if (counters) {
+      atomicAdd(&counters[0], (unsigned long long)jv);
+      atomicAdd(&counters[1], (unsigned long long)base);
+    }
+  }
+}
+
+constexpr int kSelMaxM = 16;  // keys per thread of the threshold selection: nK <= 4096
 
 // LDS of the threshold selection: the row's candidates as (order key, block index)
 // pairs, ranked by a bitonic sort.
@@ -245,17 +506,18 @@ __device__ double block_excl_scan(double x, double* part, double& total) {
   return before + (incl - x);
 }
 
-template <bool CDF>
-__global__ __launch_bounds__(256) void select_kernel(const double* scores, const double* qsim,
-                                                     const double* ksim, Dims d, int causal,
-                                                     SelectParams sp, uint8_t* mask_out,
-                                                     uint16_t* lists, int* counts,
-                                                     unsigned long long* counters) {
-  __shared__ unsigned int hist[256];
+// Threshold selection, one workgroup of 256 threads per block row (b, h, i):
+// thread t holds the keys of blocks j = t + 256m in registers; the candidates are
+// ranked by a bitonic sort of (key, block) pairs in LDS, their softmax weights are
+// summed in rank order, and the kept prefix is written in ascending block order
+// (ballots, then a prefix over the four waves).
+__global__ __launch_bounds__(256) void select_cdf_kernel(const double* scores, const double* qsim,
+                                                         const double* ksim, Dims d, int causal,
+                                                         SelectParams sp, uint8_t* mask_out,
+                                                         uint16_t* lists, int* counts,
+                                                         unsigned long long* counters) {
   __shared__ int sh_int[4][2];
-  __shared__ int sh_sel[2];
-  __shared__ unsigned long long sh_key;
-  __shared__ std::conditional_t<CDF, CdfLds, char> cdf_lds;
+  __shared__ CdfLds cdf_lds;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.x;
   const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
@@ -301,145 +563,79 @@ __global__ __launch_bounds__(256) void select_kernel(const double* scores, const
   __syncthreads();
   const int C = sh_int[0][0] + sh_int[1][0] + sh_int[2][0] + sh_int[3][0];
   __syncthreads();   // sh_int is reused below
-  unsigned long long T = 0ull, pmask = 0ull;
+  unsigned long long T = 0ull;
   int need = 0;
-  int kk;
-  if constexpr (CDF) {
-    kk = 0;
-    if (C > 0) {
-      // rank the candidates: bitonic sort of (key, j) over the first n2 >= jv slots
-      // (non-candidates and padding carry key 0 and sort last)
-      CdfLds& L = cdf_lds;
-      int n2 = 64;
-      while (n2 < jv) n2 <<= 1;
-      for (int m = tid; m < n2; m += 256) {   // slot m starts as block m
-        L.key[m] = 0ull;
-        L.j[m] = (unsigned short)m;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < kSelMaxM; ++m) {
-        const int j = tid + 256 * m;
-        if (((candm >> m) & 1u)) L.key[j] = key[m];
-      }
-      __syncthreads();
-      for (int kb = 2; kb <= n2; kb <<= 1) {
-        for (int jj = kb >> 1; jj > 0; jj >>= 1) {
-          for (int idx = tid; idx < (n2 >> 1); idx += 256) {
-            const int a = 2 * jj * (idx / jj) + (idx % jj), b = a + jj;
-            const unsigned long long ka = L.key[a], kb2 = L.key[b];
-            const int ja = L.j[a], jb = L.j[b];
-            const bool a_first = ranks_before(ka, ja, kb2, jb);
-            const bool up = (a & kb) == 0;   // this run is ordered best-first
-            if (up ? !a_first : a_first) {
-              L.key[a] = kb2;
-              L.key[b] = ka;
-              L.j[a] = (unsigned short)jb;
-              L.j[b] = (unsigned short)ja;
-            }
-          }
-          __syncthreads();
-        }
-      }
-      // softmax weights e_m = exp(s_(m) - s_(0)) of the first C ranks, a prefix sum
-      // in rank order (thread t owns ranks 16t .. 16t+15), and the count of ranks
-      // whose cumulative weight stays below tau * total
-      const double smax = srow[L.j[0]];
-      double e[kSelMaxM], run = 0.0;
-#pragma unroll
-      for (int m = 0; m < kSelMaxM; ++m) {
-        const int r = kSelMaxM * tid + m;
-        e[m] = r < C ? exp(srow[L.j[r]] - smax) : 0.0;
-        run += e[m];
-      }
-      double total;
-      double pre = block_excl_scan(run, L.part, total);
-      const double lim = sel * total;
-      int below = 0;
-#pragma unroll
-      for (int m = 0; m < kSelMaxM; ++m) {
-        const int r = kSelMaxM * tid + m;
-        pre += e[m];
-        below += (r < C && pre < lim) ? 1 : 0;
-      }
-      for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, 64);
-      if (lane == 0) L.cnt[wv] = below;
-      __syncthreads();
-      kk = min(C, 1 + L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3]);
-      // the threshold key and how many of the equal keys the prefix takes
-      T = L.key[kk - 1];
-      int eq = 0;
-      for (int r = tid; r < kk; r += 256) eq += (L.key[r] == T) ? 1 : 0;
-      for (int off = 32; off >= 1; off >>= 1) eq += __shfl_xor(eq, off, 64);
-      __syncthreads();
-      if (lane == 0) L.cnt[wv] = eq;
-      __syncthreads();
-      need = L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3];
-      __syncthreads();
+  int kk = 0;
+  if (C > 0) {
+    // rank the candidates: bitonic sort of (key, j) over the first n2 >= jv slots
+    // (non-candidates and padding carry key 0 and sort last)
+    CdfLds& L = cdf_lds;
+    int n2 = 64;
+    while (n2 < jv) n2 <<= 1;
+    for (int m = tid; m < n2; m += 256) {   // slot m starts as block m
+      L.key[m] = 0ull;
+      L.j[m] = (unsigned short)m;
     }
-  } else {
-    kk = keep_count(C, sel);
-  }
-  if (!CDF && kk > 0) {
-    int krem = kk;  // rank still to be located among keys matching the prefix
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      hist[tid] = 0u;
-      __syncthreads();
+    __syncthreads();
 #pragma unroll
-      for (int m = 0; m < kSelMaxM; ++m)
-        if (((candm >> m) & 1u) && (key[m] & pmask) == T)
-          atomicAdd(&hist[(unsigned int)(key[m] >> shift) & 255u], 1u);
-      __syncthreads();
-      if (wv == 0) {
-        // lane l owns digits 255-4l .. 252-4l (descending); suffix counts by scan
-        unsigned int c[4], tot = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = hist[255 - (4 * lane + e)];
-          tot += c[e];
-        }
-        unsigned int incl = tot;
-        for (int off = 1; off < 64; off <<= 1) {
-          const unsigned int y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        unsigned int run = incl - tot;  // keys with a larger digit than this lane's range
-        int found = -1;
-        unsigned int above = 0u, here = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (found < 0 && run + c[e] >= (unsigned int)krem) {
-            found = 255 - (4 * lane + e);
-            above = run;
-            here = c[e];
+    for (int m = 0; m < kSelMaxM; ++m) {
+      const int j = tid + 256 * m;
+      if (((candm >> m) & 1u)) L.key[j] = key[m];
+    }
+    __syncthreads();
+    for (int kb = 2; kb <= n2; kb <<= 1) {
+      for (int jj = kb >> 1; jj > 0; jj >>= 1) {
+        for (int idx = tid; idx < (n2 >> 1); idx += 256) {
+          const int a = 2 * jj * (idx / jj) + (idx % jj), b = a + jj;
+          const unsigned long long ka = L.key[a], kb2 = L.key[b];
+          const int ja = L.j[a], jb = L.j[b];
+          const bool a_first = ranks_before(ka, ja, kb2, jb);
+          const bool up = (a & kb) == 0;   // this run is ordered best-first
+          if (up ? !a_first : a_first) {
+            L.key[a] = kb2;
+            L.key[b] = ka;
+            L.j[a] = (unsigned short)jb;
+            L.j[b] = (unsigned short)ja;
           }
-          run += c[e];
         }
-        const unsigned long long fm = __ballot(found >= 0);
-        const int src = __ffsll((long long)fm) - 1;
-        if (lane == src) {
-          sh_sel[0] = found;
-          sh_sel[1] = (int)above;
-          sh_int[0][1] = (int)here;  // keys matching the extended prefix
-        }
-      }
-      __syncthreads();
-      T |= (unsigned long long)sh_sel[0] << shift;
-      pmask |= 255ull << shift;
-      krem -= sh_sel[1];
-      if (sh_int[0][1] == 1 && pass < 7) {
-        // a single key matches: it is the threshold
-#pragma unroll
-        for (int m = 0; m < kSelMaxM; ++m)
-          if (((candm >> m) & 1u) && (key[m] & pmask) == T) sh_key = key[m];
         __syncthreads();
-        T = sh_key;
-        break;
       }
-      __syncthreads();  // hist and sh_sel are rewritten by the next pass
     }
-    need = krem;  // keys equal to T still to take (lowest block index first)
+    // softmax weights e_m = exp(s_(m) - s_(0)) of the first C ranks, a prefix sum
+    // in rank order (thread t owns ranks 16t .. 16t+15), and the count of ranks
+    // whose cumulative weight stays below tau * total
+    const double smax = srow[L.j[0]];
+    double e[kSelMaxM], run = 0.0;
+#pragma unroll
+    for (int m = 0; m < kSelMaxM; ++m) {
+      const int r = kSelMaxM * tid + m;
+      e[m] = r < C ? exp(srow[L.j[r]] - smax) : 0.0;
+      run += e[m];
+    }
+    double total;
+    double pre = block_excl_scan(run, L.part, total);
+    const double lim = sel * total;
+    int below = 0;
+#pragma unroll
+    for (int m = 0; m < kSelMaxM; ++m) {
+      const int r = kSelMaxM * tid + m;
+      pre += e[m];
+      below += (r < C && pre < lim) ? 1 : 0;
+    }
+    for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, 64);
+    if (lane == 0) L.cnt[wv] = below;
+    __syncthreads();
+    kk = min(C, 1 + L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3]);
+    // the threshold key and how many of the equal keys the prefix takes
+    T = L.key[kk - 1];
+    int eq = 0;
+    for (int r = tid; r < kk; r += 256) eq += (L.key[r] == T) ? 1 : 0;
+    for (int off = 32; off >= 1; off >>= 1) eq += __shfl_xor(eq, off, 64);
+    __syncthreads();
+    if (lane == 0) L.cnt[wv] = eq;
+    __syncthreads();
+    need = L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3];
+    __syncthreads();
   }
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_before = 0, base = 0;
@@ -595,13 +791,24 @@ hipError_t launch_select(const double* scores, const double* qsim, const double*
                          uint16_t* lists, int* counts, unsigned long long* counters,
                          hipStream_t s) {
   if (d.nK > 256 * kSelMaxM) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((int64_t)d.B * d.H * d.nQ));
-  if (sp.cdf)
-    select_kernel<true><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists,
-                                             counts, counters);
-  else
-    select_kernel<false><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists,
-                                              counts, counters);
+  const int64_t rows = (int64_t)d.B * d.H * d.nQ;
+  if (sp.cdf) {
+    select_cdf_kernel<<<dim3((unsigned)rows), 256, 0, s>>>(scores, qsim, ksim, d, causal, sp,
+                                                           mask_out, lists, counts, counters);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((rows + 3) / 4));
+#define SPARGE_TOPK(MKV) \
+  select_topk_kernel<MKV><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists, \
+                                               counts, counters)
+  if (d.nK <= 64) SPARGE_TOPK(1);
+  else if (d.nK <= 128) SPARGE_TOPK(2);
+  else if (d.nK <= 256) SPARGE_TOPK(4);
+  else if (d.nK <= 512) SPARGE_TOPK(8);
+  else if (d.nK <= 1024) SPARGE_TOPK(16);
+  else if (d.nK <= 2048) SPARGE_TOPK(32);
+  else SPARGE_TOPK(64);
+#undef SPARGE_TOPK
   return hipGetLastError();
 }
 

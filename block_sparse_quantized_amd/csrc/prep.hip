@@ -43,6 +43,25 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// Sum of v over each group of G consecutive lanes (G = 8 or 16), returned to every
+// lane of the group, by DPP lane swaps: partner lane^1, lane^2 (quad permutes),
+// the mirrored lane of the 8-lane half, then of the 16-lane row.
+template <int DPP>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(b & 0xffffffffll), DPP, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), DPP, 0xf, 0xf, true);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+template <int G>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  v = v + dpp_f64<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+  v = v + dpp_f64<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+  v = v + dpp_f64<0x141>(v);   // row_half_mirror
+  if constexpr (G == 16) v = v + dpp_f64<0x140>(v);   // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ signed char quant_code(float x, float inv) {
   float c = __builtin_rintf(x * inv);
   c = fminf(fmaxf(c, -127.0f), 127.0f);
@@ -141,27 +160,36 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
   }
 
   // Row norms of the tile held in x[] (1/||x_r||, 0 for a zero row) into inv_s, and
-  // the tile into LDS.
+  // the tile into LDS.  The CH lanes holding a row's chunks sum their squares across
+  // the lane group (every lane gets the same total: each step adds two partial sums,
+  // and addition commutes); then lane ch < NCH of each group takes the square root
+  // and the division for chunk ch, so each row pays for them once.  The squares of
+  // 16-bit inputs are exact in fp64, so the fused multiply-adds round exactly as a
+  // product and a sum would.
   auto stage = [&](const uint4 (&x)[NCH]) {
+    const int ch = tid % CH;
+    double tot[NCH];
 #pragma unroll
     for (int kk = 0; kk < NCH; ++kk) {
-      const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
+      const int e = tid + 256 * kk, row = e / CH;
       const unsigned int wd[4] = {x[kk].x, x[kk].y, x[kk].z, x[kk].w};
       double ss = 0.0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const double lo = u16_to_f32((unsigned short)(wd[c] & 0xffffu), F16);
         const double hi = u16_to_f32((unsigned short)(wd[c] >> 16), F16);
-        ss = ss + lo * lo;
-        ss = ss + hi * hi;
+        ss = fma(lo, lo, ss);
+        ss = fma(hi, hi, ss);
       }
-#pragma unroll
-      for (int m = 1; m < CH; m <<= 1) ss = ss + shfl_xor_f64(ss, m);
-      if (ch == 0) {
-        const double nrm = sqrt(ss);
-        inv_s[row] = nrm > 0.0 ? 1.0 / nrm : 0.0;
-      }
+      tot[kk] = group_sum_f64<CH>(ss);
       *(uint4*)(tile + row * ROWB + 16 * ch) = x[kk];
+    }
+    if (ch < NCH) {
+      double ss = tot[0];
+#pragma unroll
+      for (int kk = 1; kk < NCH; ++kk) ss = (ch == kk) ? tot[kk] : ss;
+      const double nrm = sqrt(ss);
+      inv_s[(tid + 256 * ch) / CH] = nrm > 0.0 ? 1.0 / nrm : 0.0;
     }
   };
   // Channel sums s and unit-row sums u of tile rows [lo, hi) for this thread's
@@ -172,7 +200,7 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
     for (int r = lo; r < hi; ++r) {
       const double x = u16_to_f32(*(const unsigned short*)(tile + r * ROWB + 2 * c), F16);
       s = s + x;
-      u = u + x * inv_s[r];
+      u = fma(x, inv_s[r], u);
     }
   };
 
@@ -195,7 +223,7 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
         S = S + part_s[pp * D + tid];
         U = U + part_u[pp * D + tid];
       }
-      qmean[((int64_t)bh * d.nQ + i) * D + tid] = S / (double)nrows;
+      qmean[mean_index(bh, pad16(d.nQ), i, tid, D)] = S / (double)nrows;
       sq = U * U;
     }
 #pragma unroll
@@ -239,7 +267,7 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
       const int j = 2 * i + fb;
       if (nb[fb] > 0) {
         const double mean = S / (double)nb[fb];
-        kmean[((int64_t)bh * d.nK + j) * D + fc] = mean;
+        kmean[mean_index(bh, pad16(d.nK), j, fc, D)] = mean;
         mean_s[fb][fc] = (float)mean;
         if constexpr (QUANT) kbar[((int64_t)bh * d.nK + j) * D + fc] = (float)mean;
       }

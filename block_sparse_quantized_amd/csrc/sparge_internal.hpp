@@ -27,6 +27,17 @@ struct Dims {
   int lstride;  // elements per kept-block list row: nK rounded up to 8 (16-byte rows)
 };
 
+// fp64 block means are stored per head in 16-row tiles (rows padded to a multiple of
+// 16), laid out for the operand reads of the fp64 pooled-score MFMAs: inside a tile,
+// row r and channel c, with kq = c / (D/4) and s = c % (D/4), sit at
+// ((s/2)*64 + kq*16 + r)*2 + s%2, so that lane kq*16 + r reads channels s and s+1 of
+// its row as one 16-byte load and a wavefront's load is 1 KB of contiguous memory.
+inline __host__ __device__ int pad16(int n) { return (n + 15) & ~15; }
+inline __host__ __device__ int64_t mean_index(int64_t bh, int rows_padded, int row, int c, int D) {
+  const int q4 = D / 4, kq = c / q4, s = c % q4;
+  return (bh * rows_padded + (row & ~15)) * D + (((s >> 1) * 64 + kq * 16 + (row & 15)) * 2 + (s & 1));
+}
+
 inline Dims make_dims(int B, int H, int N, int D) {
   Dims d;
   d.B = B; d.H = H; d.N = N; d.D = D;
@@ -40,7 +51,8 @@ inline Dims make_dims(int B, int H, int N, int D) {
 // Workspace: one buffer, carved into 256-byte aligned regions.
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t qmean, qsim, kmean, ksim; // fp64 block means and self-similarities
+  size_t qmean, qsim, kmean, ksim; // fp64 block means (tiled, see mean_index) and
+                                   // self-similarities
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
   size_t lists, counts;            // uint16 kept-block lists (BH, nQ, lstride), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
