@@ -12,8 +12,6 @@
 //     plus every valid block of a non-similar row or column.
 // All arithmetic that decides the mask runs in IEEE fp64 with no fused
 // multiply-adds outside the dot products, following the reference steps.
-#include <type_traits>
-
 #include "sparge_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -283,42 +281,80 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
   return wave_allreduce_u64(v, [](unsigned long long x, unsigned long long y) { return y < x ? y : x; });
 }
-// Inclusive prefix sum over the lanes in lane order: shifts by 1, 2, 4 and 8 inside
+// Inclusive prefix sums over the lanes in lane order: shifts by 1, 2, 4 and 8 inside
 // each row (lanes without a source add 0), then the last lane of row 0 (and of row
 // 2) added to row 1 (row 3), then lane 31 added to rows 2 and 3.
-__device__ __forceinline__ unsigned int wave_incl_scan_u32(unsigned int v) {
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
-  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned int dpp_shift_u32(unsigned int v) {
+  return (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_shift_u64(unsigned long long v) {
+  const unsigned long long lo = dpp_shift_u32<CTRL, ROWS>((unsigned int)v);
+  const unsigned long long hi = dpp_shift_u32<CTRL, ROWS>((unsigned int)(v >> 32));
+  return (hi << 32) | lo;
+}
+template <class T, class SH>
+__device__ __forceinline__ T wave_incl_scan(T v, SH) {
+  v += SH::template f<0x111, 0xf>(v);   // row_shr:1
+  v += SH::template f<0x112, 0xf>(v);   // row_shr:2
+  v += SH::template f<0x114, 0xf>(v);   // row_shr:4
+  v += SH::template f<0x118, 0xf>(v);   // row_shr:8
+  v += SH::template f<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += SH::template f<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
   return v;
 }
+struct ShiftU32 {
+  template <int CTRL, int ROWS> __device__ static unsigned int f(unsigned int v) { return dpp_shift_u32<CTRL, ROWS>(v); }
+};
+struct ShiftU64 {
+  template <int CTRL, int ROWS> __device__ static unsigned long long f(unsigned long long v) {
+    return dpp_shift_u64<CTRL, ROWS>(v);
+  }
+};
+__device__ __forceinline__ unsigned int wave_incl_scan_u32(unsigned int v) { return wave_incl_scan(v, ShiftU32{}); }
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  return wave_incl_scan(v, ShiftU64{});
+}
 
-// Top-k selection, one wavefront per block row (b, h, i), four rows per workgroup
+// Block selection, one wavefront per block row (b, h, i), four rows per workgroup
 // and no workgroup barriers.  Lane l holds the keys of blocks j = l + 64m (m < MK,
-// nK <= 64 MK), so every chunk m is 64 consecutive blocks in lane order.  The
-// k-th largest candidate key is located exactly by a radix select over 8-bit
-// digits: the leading bits shared by every candidate (from the wave's smallest and
-// largest key) are skipped, then each pass histograms the keys that match the
-// prefix found so far in the wavefront's own LDS bins and walks the bins from the
-// largest digit, stopping as soon as a single key matches.  Rows whose Q block is
-// not similar keep every valid block, so they skip the search.  Ties at the
-// threshold go to the lowest block indices; kept blocks are written in ascending
+// nK <= 64 MK), so every chunk m is 64 consecutive blocks in lane order.  The key T
+// of the last kept rank is located exactly by a radix search over 8-bit digits: the
+// leading bits shared by every candidate (from the wave's smallest and largest key)
+// are skipped, then each pass histograms the keys that match the prefix found so
+// far in the wavefront's own LDS bins and walks the bins from the largest digit,
+// stopping as soon as a single key matches.
+//   * top-k: the bins count keys; T is the key of rank k_i.
+//   * threshold (CDF): the bins also sum the keys' softmax weights exp(s - s_max),
+//     held as integers in units of 2^-51, so the sums are exact whatever order the
+//     atomic adds land in; T is the key of the first rank whose cumulative weight
+//     reaches tau times the total.
+// Rows whose Q block is not similar keep every valid block, so they skip the search.
+// Ties at T go to the lowest block indices; kept blocks are written in ascending
 // order (one ballot per chunk).
-template <int MK>
-__global__ __launch_bounds__(256) void select_topk_kernel(const double* scores, const double* qsim,
+constexpr int kSelMaxNK = 4096;   // 64 keys per lane
+
+// inverse of order_key
+__device__ __forceinline__ double key_to_double(unsigned long long k) {
+  const unsigned long long b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+template <int MK, bool CDF>
+__global__ __launch_bounds__(256) void select_wave_kernel(const double* scores, const double* qsim,
                                                           const double* ksim, Dims d, int causal,
                                                           SelectParams sp, uint8_t* mask_out,
                                                           uint16_t* lists, int* counts,
                                                           unsigned long long* counters) {
   __shared__ __attribute__((aligned(16))) unsigned int hist_s[4][256];
+  __shared__ __attribute__((aligned(16))) unsigned long long whist_s[4][CDF ? 256 : 2];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   // no workgroup barriers in this kernel, so a wavefront past the end may leave
   if (row >= (int64_t)d.B * d.H * d.nQ) return;
   unsigned int* hist = hist_s[wv];
+  unsigned long long* whist = whist_s[wv];
   const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
   const int h = bh % d.H;
   const double theta = sp.head_theta ? sp.head_theta[h] : sp.theta;
@@ -363,23 +399,54 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const double* scores, 
     for (int m = 0; m < MK; ++m) key[m] = order_key(sv[m]) & (0ull - ((candm >> m) & 1ull));
   }
   const int C = wave_sum_i32(__popcll(candm));
-  const int kk = keep_count(C, sel);
+  auto is_cand = [&](int m) { return 64 * m < jv && ((candm >> m) & 1ull); };
 
   unsigned long long T = 0ull;
-  int need = 0;
-  if (simq && kk > 0) {
+  int need = 0, kk = 0;
+  if (simq && C > 0) {
     unsigned long long kmax = 0ull, kmin = ~0ull;
 #pragma unroll
     for (int m = 0; m < MK; ++m)
-      if (64 * m < jv && ((candm >> m) & 1ull)) {
+      if (is_cand(m)) {
         kmax = key[m] > kmax ? key[m] : kmax;
         kmin = key[m] < kmin ? key[m] : kmin;
       }
     kmax = wave_max_u64(kmax);
     kmin = wave_min_u64(kmin);
-    int krem = kk;   // rank still to be located among the keys matching the prefix
-    if (kmax == kmin) {
-      T = kmax;      // every candidate has the same key
+    int krem = 0;                        // top-k: rank still to locate among prefix matches
+    int n_above = 0;                     // CDF: candidates above the prefix
+    unsigned long long A = 0ull;         // CDF: their weight
+    unsigned long long target = 0ull;    // CDF: tau times the total weight
+    unsigned long long wt[CDF ? MK : 1];
+    bool found_t = false;
+    if constexpr (CDF) {
+      const double smax = key_to_double(kmax);
+      unsigned long long zl = 0ull;
+#pragma unroll
+      for (int m = 0; m < MK; ++m) {
+        wt[m] = 0ull;
+        if (64 * m < jv) {   // chunks past the causal limit hold no candidate
+          const double e = exp(key_to_double(key[m]) - smax);
+          wt[m] = is_cand(m) ? (unsigned long long)(e * 0x1p51) : 0ull;
+        }
+        zl += wt[m];
+      }
+      const unsigned long long Z =
+          wave_allreduce_u64(zl, [](unsigned long long x, unsigned long long y) { return x + y; });
+      target = sel >= 1.0 ? Z : __umul64hi((unsigned long long)(sel * 0x1p64), Z);
+      if (target == 0ull) {              // the first rank already reaches it
+        T = kmax;
+        found_t = true;
+      }
+    } else {
+      kk = keep_count(C, sel);
+      krem = kk;
+    }
+    int n_t = C;                         // keys equal to T (all of them when kmax == kmin)
+    if (found_t) {
+      n_t = 1;
+    } else if (kmax == kmin) {
+      T = kmax;                          // every candidate has the same key
     } else {
       // bytes above the highest differing bit are common to all candidates
       const int top = (63 - __clzll((long long)(kmax ^ kmin))) >> 3;
@@ -388,52 +455,100 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const double* scores, 
       for (int byte = top; byte >= 0; --byte) {
         const int shift = 8 * byte;
         *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (CDF) {
+          *(uint4*)(whist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+          *(uint4*)(whist + 4 * lane + 2) = make_uint4(0u, 0u, 0u, 0u);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int m = 0; m < MK; ++m)
-          if (64 * m < jv && ((candm >> m) & 1ull) && (key[m] & pmask) == T)
-            atomicAdd(&hist[(unsigned int)(key[m] >> shift) & 255u], 1u);
+          if (is_cand(m) && (key[m] & pmask) == T) {
+            const unsigned int dg = (unsigned int)(key[m] >> shift) & 255u;
+            atomicAdd(&hist[dg], 1u);
+            if constexpr (CDF) atomicAdd(&whist[dg], wt[m]);
+          }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane l owns digits 255-4l .. 252-4l (descending); counts above it by a scan
+        // lane l owns digits 255-4l .. 252-4l (descending); counts and weights above
+        // it by scans over the lanes
         const uint4 cv = *(const uint4*)(hist + 252 - 4 * lane);
         const unsigned int c[4] = {cv.w, cv.z, cv.y, cv.x};
         const unsigned int tot = c[0] + c[1] + c[2] + c[3];
         unsigned int run = wave_incl_scan_u32(tot) - tot;
+        unsigned long long w4[4] = {0ull, 0ull, 0ull, 0ull}, wrun = 0ull;
+        if constexpr (CDF) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = whist[255 - 4 * lane - e];
+          const unsigned long long wtot = (w4[0] + w4[1]) + (w4[2] + w4[3]);
+          wrun = wave_incl_scan_u64(wtot) - wtot;
+        }
         int found = -1;
         unsigned int above = 0u, here = 0u;
+        unsigned long long wabove = 0ull;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (found < 0 && run + c[e] >= (unsigned int)krem) {
+          const bool hit = CDF ? (c[e] > 0u && A + wrun + w4[e] >= target) : (run + c[e] >= (unsigned int)krem);
+          if (found < 0 && hit) {
             found = 255 - (4 * lane + e);
             above = run;
             here = c[e];
+            wabove = wrun;
           }
           run += c[e];
+          wrun += w4[e];
         }
         const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(found >= 0)) - 1);
         const int digit = __builtin_amdgcn_readlane(found, src);
-        krem -= __builtin_amdgcn_readlane((int)above, src);
+        const int n_hi = __builtin_amdgcn_readlane((int)above, src);
         const unsigned int nhere = (unsigned int)__builtin_amdgcn_readlane((int)here, src);
+        if constexpr (CDF) {
+          A += ((unsigned long long)(unsigned int)__builtin_amdgcn_readlane((int)(wabove >> 32), src) << 32) |
+               (unsigned int)__builtin_amdgcn_readlane((int)(unsigned int)wabove, src);
+          n_above += n_hi;
+        } else {
+          krem -= n_hi;
+        }
         // every lane has finished reading the bins before the next pass clears them
         __builtin_amdgcn_wave_barrier();
         T |= (unsigned long long)digit << shift;
         pmask |= 255ull << shift;
+        n_t = (int)nhere;
         if (nhere == 1u && byte > 0) {
-          // a single key matches the prefix: it is the threshold
+          // a single key matches the prefix: it is T
           unsigned long long mine = 0ull;
 #pragma unroll
           for (int m = 0; m < MK; ++m)
-            if (64 * m < jv && ((candm >> m) & 1ull) && (key[m] & pmask) == T) mine = key[m];
+            if (is_cand(m) && (key[m] & pmask) == T) mine = key[m];
           T = wave_max_u64(mine);
           break;
         }
       }
     }
-    need = krem;   // keys equal to T still to take, lowest block index first
+    if constexpr (CDF) {
+      if (found_t) {
+        need = 1;
+        kk = 1;
+      } else {
+        // the n_t keys equal to T share one weight w; in rank order the q-th of them
+        // ends at cumulative weight A + q w, so the first to reach the target is
+        // q = ceil((target - A) / w) (target > A > ... and A + n_t w >= target)
+        unsigned long long mine = 0ull;
+#pragma unroll
+        for (int m = 0; m < MK; ++m)
+          if (is_cand(m) && key[m] == T) mine = wt[m];
+        const unsigned long long w = wave_max_u64(mine);
+        const unsigned long long gap = target - A;
+        unsigned long long q = w > 0ull ? (gap + w - 1ull) / w : 1ull;
+        q = q < 1ull ? 1ull : (q > (unsigned long long)n_t ? (unsigned long long)n_t : q);
+        need = (int)q;
+        kk = n_above + need;
+      }
+    } else {
+      need = krem;   // keys equal to T still to take, lowest block index first
+    }
   }
 
   const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -463,226 +578,6 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const double* scores, 
     }
   }
   if (lane == 0) {
-    counts[row] = base;
-    if (counters) {
-      atomicAdd(&counters[0], (unsigned long long)jv);
-      atomicAdd(&counters[1], (unsigned long long)base);
-    }
-  }
-}
-
-constexpr int kSelMaxM = 16;  // keys per thread of the threshold selection: nK <= 4096
-
-// LDS of the threshold selection: the row's candidates as (order key, block index)
-// pairs, ranked by a bitonic sort.
-struct CdfLds {
-  unsigned long long key[kSelMaxM * 256];
-  unsigned short j[kSelMaxM * 256];
-  double part[4];
-  int cnt[4];
-};
-
-// a ranks before b: larger score first, then the lower block index
-__device__ __forceinline__ bool ranks_before(unsigned long long ka, int ja, unsigned long long kb, int jb) {
-  return ka > kb || (ka == kb && ja < jb);
-}
-
-// Block-wide exclusive prefix of one double per thread, in thread order (fixed
-// association: a wavefront scan, then the four wavefront totals in order); also
-// returns the total.  Every thread must call it.
-__device__ double block_excl_scan(double x, double* part, double& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  double incl = x;
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) part[wv] = incl;
-  __syncthreads();
-  double before = 0.0;
-  for (int w2 = 0; w2 < wv; ++w2) before += part[w2];
-  total = ((part[0] + part[1]) + part[2]) + part[3];
-  __syncthreads();
-  return before + (incl - x);
-}
-
-// Threshold selection, one workgroup of 256 threads per block row (b, h, i):
-// thread t holds the keys of blocks j = t + 256m in registers; the candidates are
-// ranked by a bitonic sort of (key, block) pairs in LDS, their softmax weights are
-// summed in rank order, and the kept prefix is written in ascending block order
-// (ballots, then a prefix over the four waves).
-__global__ __launch_bounds__(256) void select_cdf_kernel(const double* scores, const double* qsim,
-                                                         const double* ksim, Dims d, int causal,
-                                                         SelectParams sp, uint8_t* mask_out,
-                                                         uint16_t* lists, int* counts,
-                                                         unsigned long long* counters) {
-  __shared__ int sh_int[4][2];
-  __shared__ CdfLds cdf_lds;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int bh = (int)(row / d.nQ), i = (int)(row % d.nQ);
-  const int h = bh % d.H;
-  const double theta = sp.head_theta ? sp.head_theta[h] : sp.theta;
-  const double sel = sp.head_sel ? sp.head_sel[h] : sp.sel;
-  const int nK = d.nK;
-  const int mk = (nK + 255) >> 8;
-  const int jv = causal ? min(nK, 2 * i + 2) : nK;
-  const bool simq = qsim[row] >= theta;
-  const double* srow = scores + row * nK;
-  const double* ks = ksim + (int64_t)bh * nK;
-
-  unsigned long long key[kSelMaxM];
-  unsigned int validm = 0u, simkm = 0u;
-  double kv[kSelMaxM];
-#pragma unroll
-  for (int m = 0; m < kSelMaxM; ++m) {
-    const int j = tid + 256 * m;
-    kv[m] = (m < mk && j < nK) ? ks[j] : 0.0;
-  }
-  double sv[kSelMaxM];
-#pragma unroll
-  for (int m = 0; m < kSelMaxM; ++m) {
-    const int j = tid + 256 * m;
-    const bool valid = m < mk && j < jv;
-    sv[m] = valid ? srow[j] : 0.0;
-    validm |= (valid ? 1u : 0u) << m;
-  }
-  int cand_local = 0;
-#pragma unroll
-  for (int m = 0; m < kSelMaxM; ++m) {
-    const int j = tid + 256 * m;
-    const bool simk = m < mk && j < nK && kv[m] >= theta;
-    simkm |= (simk ? 1u : 0u) << m;
-    const bool cand = ((validm >> m) & 1u) && simk;
-    key[m] = cand ? order_key(sv[m]) : 0ull;
-    cand_local += cand ? 1 : 0;
-  }
-  const unsigned int candm = validm & simkm;
-  for (int off = 32; off >= 1; off >>= 1) cand_local += __shfl_xor(cand_local, off, 64);
-  if (lane == 0) sh_int[wv][0] = cand_local;
-  __syncthreads();
-  const int C = sh_int[0][0] + sh_int[1][0] + sh_int[2][0] + sh_int[3][0];
-  __syncthreads();   // sh_int is reused below
-  unsigned long long T = 0ull;
-  int need = 0;
-  int kk = 0;
-  if (C > 0) {
-    // rank the candidates: bitonic sort of (key, j) over the first n2 >= jv slots
-    // (non-candidates and padding carry key 0 and sort last)
-    CdfLds& L = cdf_lds;
-    int n2 = 64;
-    while (n2 < jv) n2 <<= 1;
-    for (int m = tid; m < n2; m += 256) {   // slot m starts as block m
-      L.key[m] = 0ull;
-      L.j[m] = (unsigned short)m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kSelMaxM; ++m) {
-      const int j = tid + 256 * m;
-      if (((candm >> m) & 1u)) L.key[j] = key[m];
-    }
-    __syncthreads();
-    for (int kb = 2; kb <= n2; kb <<= 1) {
-      for (int jj = kb >> 1; jj > 0; jj >>= 1) {
-        for (int idx = tid; idx < (n2 >> 1); idx += 256) {
-          const int a = 2 * jj * (idx / jj) + (idx % jj), b = a + jj;
-          const unsigned long long ka = L.key[a], kb2 = L.key[b];
-          const int ja = L.j[a], jb = L.j[b];
-          const bool a_first = ranks_before(ka, ja, kb2, jb);
-          const bool up = (a & kb) == 0;   // this run is ordered best-first
-          if (up ? !a_first : a_first) {
-            L.key[a] = kb2;
-            L.key[b] = ka;
-            L.j[a] = (unsigned short)jb;
-            L.j[b] = (unsigned short)ja;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    // softmax weights e_m = exp(s_(m) - s_(0)) of the first C ranks, a prefix sum
-    // in rank order (thread t owns ranks 16t .. 16t+15), and the count of ranks
-    // whose cumulative weight stays below tau * total
-    const double smax = srow[L.j[0]];
-    double e[kSelMaxM], run = 0.0;
-#pragma unroll
-    for (int m = 0; m < kSelMaxM; ++m) {
-      const int r = kSelMaxM * tid + m;
-      e[m] = r < C ? exp(srow[L.j[r]] - smax) : 0.0;
-      run += e[m];
-    }
-    double total;
-    double pre = block_excl_scan(run, L.part, total);
-    const double lim = sel * total;
-    int below = 0;
-#pragma unroll
-    for (int m = 0; m < kSelMaxM; ++m) {
-      const int r = kSelMaxM * tid + m;
-      pre += e[m];
-      below += (r < C && pre < lim) ? 1 : 0;
-    }
-    for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, 64);
-    if (lane == 0) L.cnt[wv] = below;
-    __syncthreads();
-    kk = min(C, 1 + L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3]);
-    // the threshold key and how many of the equal keys the prefix takes
-    T = L.key[kk - 1];
-    int eq = 0;
-    for (int r = tid; r < kk; r += 256) eq += (L.key[r] == T) ? 1 : 0;
-    for (int off = 32; off >= 1; off >>= 1) eq += __shfl_xor(eq, off, 64);
-    __syncthreads();
-    if (lane == 0) L.cnt[wv] = eq;
-    __syncthreads();
-    need = L.cnt[0] + L.cnt[1] + L.cnt[2] + L.cnt[3];
-    __syncthreads();
-  }
-  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int eq_before = 0, base = 0;
-  uint8_t* mrow = mask_out ? mask_out + row * nK : nullptr;
-  uint16_t* lrow = lists + row * d.lstride;
-#pragma unroll
-  for (int m = 0; m < kSelMaxM; ++m) {
-    if (m < mk) {
-      const int j = tid + 256 * m;
-      const bool valid = (validm >> m) & 1u, simk = (simkm >> m) & 1u;
-      const bool cand = valid && simk;
-      const bool is_eq = cand && kk > 0 && key[m] == T;
-      const unsigned long long eqm = __ballot(is_eq);
-      const bool gt = cand && kk > 0 && key[m] > T;
-      const bool keep_pre = valid && (!simq || !simk || gt);
-      // ranks of the equal keys and positions of the kept blocks across the waves
-      if (lane == 0) {
-        sh_int[wv][0] = __popcll(eqm);
-      }
-      __syncthreads();
-      int eq_w = 0, eq_all = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int cw = sh_int[w2][0];
-        eq_w += (w2 < wv) ? cw : 0;
-        eq_all += cw;
-      }
-      const int rank = eq_before + eq_w + __popcll(eqm & lt_mask);
-      const bool keep = keep_pre || (is_eq && rank < need);
-      if (mrow && j < nK) mrow[j] = keep ? 1 : 0;
-      const unsigned long long km = __ballot(keep);
-      if (lane == 0) sh_int[wv][1] = __popcll(km);
-      __syncthreads();
-      int k_w = 0, k_all = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int cw = sh_int[w2][1];
-        k_w += (w2 < wv) ? cw : 0;
-        k_all += cw;
-      }
-      if (keep) lrow[base + k_w + __popcll(km & lt_mask)] = (uint16_t)j;
-      base += k_all;
-      eq_before += eq_all;
-      __syncthreads();  // sh_int is rewritten by the next chunk
-    }
-  }
-  if (tid == 0) {
     counts[row] = base;
     if (counters) {
       atomicAdd(&counters[0], (unsigned long long)jv);
@@ -790,25 +685,26 @@ hipError_t launch_select(const double* scores, const double* qsim, const double*
                          const Dims& d, int causal, const SelectParams& sp, uint8_t* mask_out,
                          uint16_t* lists, int* counts, unsigned long long* counters,
                          hipStream_t s) {
-  if (d.nK > 256 * kSelMaxM) return hipErrorInvalidValue;
+  if (d.nK > kSelMaxNK) return hipErrorInvalidValue;
   const int64_t rows = (int64_t)d.B * d.H * d.nQ;
-  if (sp.cdf) {
-    select_cdf_kernel<<<dim3((unsigned)rows), 256, 0, s>>>(scores, qsim, ksim, d, causal, sp,
-                                                           mask_out, lists, counts, counters);
-    return hipGetLastError();
-  }
   const dim3 grid((unsigned)((rows + 3) / 4));
-#define SPARGE_TOPK(MKV) \
-  select_topk_kernel<MKV><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp, mask_out, lists, \
-                                               counts, counters)
-  if (d.nK <= 64) SPARGE_TOPK(1);
-  else if (d.nK <= 128) SPARGE_TOPK(2);
-  else if (d.nK <= 256) SPARGE_TOPK(4);
-  else if (d.nK <= 512) SPARGE_TOPK(8);
-  else if (d.nK <= 1024) SPARGE_TOPK(16);
-  else if (d.nK <= 2048) SPARGE_TOPK(32);
-  else SPARGE_TOPK(64);
-#undef SPARGE_TOPK
+#define SPARGE_SEL(MKV)                                                                         \
+  do {                                                                                          \
+    if (sp.cdf)                                                                                 \
+      select_wave_kernel<MKV, true><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp,     \
+                                                         mask_out, lists, counts, counters);    \
+    else                                                                                        \
+      select_wave_kernel<MKV, false><<<grid, 256, 0, s>>>(scores, qsim, ksim, d, causal, sp,    \
+                                                          mask_out, lists, counts, counters);   \
+  } while (0)
+  if (d.nK <= 64) SPARGE_SEL(1);
+  else if (d.nK <= 128) SPARGE_SEL(2);
+  else if (d.nK <= 256) SPARGE_SEL(4);
+  else if (d.nK <= 512) SPARGE_SEL(8);
+  else if (d.nK <= 1024) SPARGE_SEL(16);
+  else if (d.nK <= 2048) SPARGE_SEL(32);
+  else SPARGE_SEL(64);
+#undef SPARGE_SEL
   return hipGetLastError();
 }
 
