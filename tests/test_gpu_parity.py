@@ -654,6 +654,25 @@ def test_max_sequence_length(dev, cdf):
     assert worst < tol
 
 
+@pytest.mark.parametrize("N", [16384, 32768, 65536])
+def test_selection_mid_sizes(dev, N):
+    """The selector's register layouts between the small tests and the full
+    workloads (rows of 4, 8 and 16 chunks of 64 K blocks): the top-k mask and the
+    threshold-selection mask against the oracle."""
+    wl = synth.workload("llm8k", H=1, N=N, D=64, seed=N % 97)
+    q, k, v = synth.make_qkv(wl, device=dev)
+    gm = bsq.sparge_predict_mask(q, k, 0.5, True)
+    _, gc = bsq.sparge_cdf_attn(q, k, v, 0.9, True, return_mask=True)
+    torch.cuda.synchronize()
+    om, infos = oracle_predict(q, k, so.OracleParams(topk=0.5, causal=True))
+    bad_topk = unexcused_mismatches(gm.cpu().numpy(), om, infos)[0]
+    oc, infc = oracle_predict(q, k, so.OracleParams(cdf=0.9, causal=True))
+    bad_cdf = cdf_mismatches(gc.cpu().numpy().astype(bool), oc, infc, 0.9)
+    say(f"selection N={N}: top-k unexcused {bad_topk} (density {om.mean():.3f}), "
+        f"cdf unexcused {bad_cdf} (density {oc.mean():.3f})")
+    assert bad_topk == 0 and bad_cdf == 0
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,variant", [("llm128k", "fp8"), ("llm8k", "cdf"), ("llm128k", "cdf")])
 def test_full_workload_variant(dev, name, variant):
