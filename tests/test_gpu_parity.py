@@ -181,6 +181,23 @@ def test_predict_mask_bit_exact(dev, N, D, causal):
         assert st["valid_blocks"] == int(sum(i["valid"].sum() for i in infos))
 
 
+@pytest.mark.parametrize("dtype,N,D", [(torch.float32, 4000, 128), (torch.float16, 4000, 128),
+                                       (torch.float32, 4000, 64)])
+def test_predict_mask_other_dtypes(dev, dtype, N, D):
+    """fp32 inputs take the separate block-statistics kernel and fp16 inputs the
+    fp16 branch of the fused preparation pass; both must give the oracle's mask on
+    the exact stored values (long enough that K blocks pass the similarity gate)."""
+    wl = synth.workload("llm8k", H=2, N=N, D=D, dtype=dtype)
+    q, k, _ = synth.make_qkv(wl, device=dev)
+    gm = bsq.sparge_predict_mask(q, k, 0.5, True)
+    om, infos = oracle_predict(q, k, so.OracleParams(topk=0.5, causal=True))
+    bad, exc = unexcused_mismatches(gm.cpu().numpy(), om, infos)
+    simk = np.mean([i["simk"].mean() for i in infos])
+    say(f"mask {dtype} N={N} D={D}: unexcused {bad}, excused {exc}, similar K blocks {simk:.2f}")
+    assert simk > 0.1
+    assert bad == 0
+
+
 def test_predict_mask_degenerate_blocks(dev):
     B, H, N, D = 1, 2, 640, 64
     q, k, _ = rand_qkv(B, H, N, D, torch.bfloat16, dev, seed=11)
