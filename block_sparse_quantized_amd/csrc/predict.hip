@@ -9,9 +9,12 @@
 //     || sum_r x_r/||x_r|| ||^2 / n^2, similar iff >= theta;
 //   * candidates of block row i: valid K blocks that are similar; row i keeps
 //     k_i = min(C, max(1, ceil(topk*C - 1e-9))) of them by (score desc, index asc),
-//     plus every valid block of a non-similar row or column.
-// All arithmetic that decides the mask runs in IEEE fp64 with no fused
-// multiply-adds outside the dot products, following the reference steps.
+//     plus every valid block of a non-similar row or column;
+//   * threshold variant ([readme] "Avalible API": the meansim calls without topk):
+//     keep the shortest prefix of that ranking whose softmax mass reaches tau.
+// All arithmetic that decides the mask runs in IEEE fp64 (fused multiply-adds only
+// inside dot products); the threshold variant sums its fp64 softmax weights as exact
+// integers in units of 2^-51.
 #include "sparge_internal.hpp"
 
 #pragma clang fp contract(off)
