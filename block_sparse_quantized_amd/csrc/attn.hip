@@ -522,7 +522,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const int lw_last = (d.lstride >> 1) - 1;
   unsigned int lw = lst32[min(1, lw_last)];
   acc_t acc_cur[2];
-  f32x16 sc_cur[2];
+  // scores of the current block, fp32 with invisible keys at -inf: two sets for the
+  // 16-bit P.V, so that the step of parity P reads one while it fills the other for
+  // the next block
+  f32x16 scA[2], scB[2];
   float mraw_cur = kNegInf;
   float ks_cur = (QK8 && cnt > 0) ? kscale_at(j_cur) : 0.0f;
   if (cnt > 0) {
@@ -532,12 +535,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     wait_vmem_all();
     __syncthreads();
     qk(s0, acc_cur);
-    mraw_cur = mask_max(acc_cur, j_cur, sc_cur);
+    mraw_cur = mask_max(acc_cur, j_cur, scA);
   }
 
   unsigned int lw_nxt = 0u;
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;        // it & 1
+    // this block's scores, and the next block's made in this step (the fp8 P.V makes
+    // them after its P.V, in place)
+    f32x16 (&sc_cur)[2] = (P && !PV8) ? scB : scA;
+    f32x16 (&sc_nxt)[2] = (P || PV8) ? scA : scB;
     std::integral_constant<int, P> sp;
     std::integral_constant<int, 1 - P> sq;
     const int j = j_cur;
@@ -600,8 +607,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       // that masked (-inf) scores stay -inf
       slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f);
     }
+    // (in a row's last step this multiplies whatever K stage 1-P holds; the result
+    // is converted below but never used)
     acc_t acc_nxt[2];
-    if (it + 1 < cnt) qk(sq, acc_nxt);
+    qk(sq, acc_nxt);
+    // 16-bit P.V: the next block's scores are converted (and their raw max taken) in
+    // quarters between the P.V MFMAs, in the same basic block, so that this work
+    // overlaps the MFMAs; masking, when the block needs it, follows the P.V
+    float mr_nxt = kNegInf;
+    auto conv_quarter = [&](auto qc) {
+      constexpr int q = decltype(qc)::value, kt = q >> 1, r0 = 8 * (q & 1);
+#pragma unroll
+      for (int r = r0; r < r0 + 8; ++r) sc_nxt[kt][r] = (float)acc_nxt[kt][r];
+#pragma unroll
+      for (int r = r0; r < r0 + 8; r += 2) mr_nxt = max3f(mr_nxt, sc_nxt[kt][r], sc_nxt[kt][r + 1]);
+    };
 
     // block max of this row in log2 units, -inf when no key is visible
     float mx;
@@ -709,11 +729,31 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
           if constexpr (dt == 0 && sg + 1 < 4) make_pw(std::integral_constant<int, sg + 1>{});
+          if constexpr (u % (kNU / 4) == 1) conv_quarter(std::integral_constant<int, u / (kNU / 4)>{});
         });
       }
       }
-    // the next block's scores: mask and max while the P.V MFMAs run
-    if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_cur);
+    // the next block's scores: mask and max (fp8 P.V: all of it here, under the
+    // MFMAs still in flight)
+    if constexpr (PV8) {
+      if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_nxt);
+    } else {
+      if (skip) static_for<0, 4>(conv_quarter);   // the P.V did not run
+      if (it + 1 < cnt) {
+        if ((64 * j_n1 + 64 > N) || (p.causal && 64 * j_n1 + 63 > wrow0) || (wrow0 + 31 >= N)) {
+          const int rel = lim - 64 * j_n1 - 8 * hf;
+          mr_nxt = kNegInf;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              sc_nxt[kt][r] = key_off2(kt, r) < rel ? sc_nxt[kt][r] : kNegInf;
+              mr_nxt = fmaxf(mr_nxt, sc_nxt[kt][r]);
+            }
+        }
+        mraw_cur = max_xor32(mr_nxt);
+      }
+    }
     j_cur = j_n1;
     j_n1 = j_n2;
     j_n2 = j_n3;
