@@ -452,7 +452,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
     koffs[s] = (unsigned int)(krow_l * KROW + 16 * ((2 * s + hf) ^ fkx<KG, PV8>(krow_l)));
-  auto qk = [&](auto kstage, acc_t (&acc)[2]) {
+  // cb(k-step) runs after each k-step's MFMAs (other work to interleave with them).
+  auto qk = [&](auto kstage, acc_t (&acc)[2], auto cb) {
     const unsigned int kb = (unsigned int)(size_t)(lds_u8_ptr)(decltype(kstage)::value ? Ks1 : Ks0);
     acc[0] = (acc_t)(0);
     acc[1] = (acc_t)(0);
@@ -477,8 +478,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kf[s % KSLOT][kt]),
                                                           q8[s], acc[kt], 0, 0, 0);
       }
+      cb(sc);
     });
   };
+  auto no_cb = [](auto) {};
 
   // Scores as fp32 with invisible keys at -inf, and the row max of the raw scores
   // (both lane halves); key of sc[kt][r] is 64j + 8hf + key_off2(kt, r), or with
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     dma_v(j_cur, s0);
     wait_vmem_all();
     __syncthreads();
-    qk(s0, acc_cur);
+    qk(s0, acc_cur, no_cb);
     mraw_cur = mask_max(acc_cur, j_cur, scA);
   }
 
@@ -607,10 +610,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       // that masked (-inf) scores stay -inf
       slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f);
     }
-    // (in a row's last step this multiplies whatever K stage 1-P holds; the result
-    // is converted below but never used)
+    // The next block's Q.K^T (in a row's last step this multiplies whatever K stage
+    // 1-P holds; the result is converted but never used).  With the 16-bit P.V it is
+    // issued below, interleaved with this block's first P fragment.
     acc_t acc_nxt[2];
-    qk(sq, acc_nxt);
+    if constexpr (PV8) qk(sq, acc_nxt, no_cb);
     // 16-bit P.V: the next block's scores are converted (and their raw max taken) in
     // quarters between the P.V MFMAs, in the same basic block, so that this work
     // overlaps the MFMAs; masking, when the block needs it, follows the P.V
@@ -706,19 +710,25 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         const float slope = QK8 ? slope_i8 : p.c;
         const float offs = (QK8 ? bias : 0.0f) - m_use;
         u32x4 pw[4];
-        auto make_pw = [&](auto kc) {
+        auto make_pw_word = [&](auto kc, auto wc) {
           constexpr int k = decltype(kc)::value, kt = k >> 1, sg = k & 1;
-  #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const int r = 8 * sg + 2 * wd;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
-            const unsigned int pr = pack2<PV_F16>(p0, p1);
-            l_acc = add_pair<PV_F16>(pr, l_acc);
-            pw[k][wd] = pr;
-          }
+          constexpr int r = 8 * sg + 2 * decltype(wc)::value;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
+          const unsigned int pr = pack2<PV_F16>(p0, p1);
+          l_acc = add_pair<PV_F16>(pr, l_acc);
+          pw[k][decltype(wc)::value] = pr;
         };
-        make_pw(std::integral_constant<int, 0>{});
+        auto make_pw = [&](auto kc) { static_for<0, 4>([&](auto wc) { make_pw_word(kc, wc); }); };
+        // words of the first P fragment after each k-step of the next block's Q.K^T
+        qk(sq, acc_nxt, [&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          static_for<0, 4>([&](auto wc) {
+            constexpr int wd = decltype(wc)::value;
+            if constexpr (wd * KSTEPS / 4 == s && (KSTEPS <= 4 || wd * KSTEPS % 4 == 0))
+              make_pw_word(std::integral_constant<int, 0>{}, wc);
+          });
+        });
         static_for<0, kNU>([&](auto uc) {
           constexpr int u = decltype(uc)::value, sg = u / DT, dt = u % DT;
           if constexpr (u + kVAhead < kNU) issue(std::integral_constant<int, u + kVAhead>{});
@@ -738,7 +748,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     if constexpr (PV8) {
       if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_nxt);
     } else {
-      if (skip) static_for<0, 4>(conv_quarter);   // the P.V did not run
+      if (skip) {   // the P.V (and the Q.K^T and conversion issued inside it) did not run
+        qk(sq, acc_nxt, no_cb);
+        static_for<0, 4>(conv_quarter);
+      }
       if (it + 1 < cnt) {
         if ((64 * j_n1 + 64 > N) || (p.causal && 64 * j_n1 + 63 > wrow0) || (wrow0 + 31 >= N)) {
           const int rel = lim - 64 * j_n1 - 8 * hf;
