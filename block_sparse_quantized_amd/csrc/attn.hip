@@ -107,6 +107,15 @@ __device__ __forceinline__ float max_xor32(float v) {
 // max that moves only when a row's running max exceeds it by more than this, so
 // O and l are rescaled rarely; P then stays below 2^8.
 constexpr float kTau = 8.0f;
+// int8 Q.K^T: the accumulators start at 0x3e22f983, the bit pattern of the MFMA's
+// inline constant 1/(2 pi).  Its mantissa field is 2292099, so for |s| below that
+// (127 * 127 * D is at most 2064512) the int32 result s + 0x3e22f983 read as a float
+// is exactly kScoreC0 + s * 2^-26, in the binade [1/8, 1/4): scores need no int to
+// float conversion, float order is integer order, and the slope and offset of the
+// exponent absorb the affine map.
+constexpr int kScoreBits = 0x3e22f983;
+constexpr float kScoreC0 = 0.15915493667125702f;   // the float with those bits
+constexpr float kScoreUnit = 67108864.0f;           // 2^26
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -440,6 +449,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const int krow_l = PV8 ? (32 * ((ql >> 2) & 1) + 4 * (ql >> 3) + (ql & 3)) : swap23(ql);
   constexpr int KTROW = PV8 ? 16 : 32;
   typedef std::conditional_t<QK8, i32x16, f32x16> acc_t;
+  static_assert(!QK8 || 127 * 127 * D < (kScoreBits & 0x7fffff), "int8 scores leave the binade");
 
   // Raw Q.K^T of the block staged in K stage KS (MFMAs only; no waits on results).
   // The K fragments of k-step s sit at row krow_l (kt = 0) and row krow_l + KTROW
@@ -453,10 +463,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   for (int s = 0; s < KSTEPS; ++s)
     koffs[s] = (unsigned int)(krow_l * KROW + 16 * ((2 * s + hf) ^ fkx<KG, PV8>(krow_l)));
   // cb(k-step) runs after each k-step's MFMAs (other work to interleave with them).
-  auto qk = [&](auto kstage, acc_t (&acc)[2], auto cb) {
+  // The scores land in sc as fp32 (int8 path: in the biased form kScoreC0 + s 2^-26).
+  auto qk = [&](auto kstage, f32x16 (&sc)[2], auto cb) {
     const unsigned int kb = (unsigned int)(size_t)(lds_u8_ptr)(decltype(kstage)::value ? Ks1 : Ks0);
-    acc[0] = (acc_t)(0);
-    acc[1] = (acc_t)(0);
+    acc_t acc[2];
+    acc[0] = (acc_t)(QK8 ? kScoreBits : 0);
+    acc[1] = acc[0];
     u32x4 kf[KSLOT][2];
     auto kissue = [&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -465,8 +477,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       kf[s % KSLOT][1] = ds_read16<KTROW * KROW>(a);
     };
     static_for<0, (KSLOT - 1 < KSTEPS ? KSLOT - 1 : KSTEPS)>(kissue);
-    static_for<0, KSTEPS>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
+    static_for<0, KSTEPS>([&](auto stc) {
+      constexpr int s = decltype(stc)::value;
       constexpr int ahead = (KSTEPS - 1 - s) < (KSLOT - 2) ? (KSTEPS - 1 - s) : (KSLOT - 2);
       lds_wait16<2 * ahead>(kf[s % KSLOT][0], kf[s % KSLOT][1]);
       if constexpr (s + KSLOT - 1 < KSTEPS) kissue(std::integral_constant<int, s + KSLOT - 1>{});
@@ -478,19 +490,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kf[s % KSLOT][kt]),
                                                           q8[s], acc[kt], 0, 0, 0);
       }
-      cb(sc);
+      cb(stc);
     });
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sc[kt] = __builtin_bit_cast(f32x16, acc[kt]);
   };
   auto no_cb = [](auto) {};
 
-  // Scores as fp32 with invisible keys at -inf, and the row max of the raw scores
-  // (both lane halves); key of sc[kt][r] is 64j + 8hf + key_off2(kt, r), or with
-  // the fp8 P.V 64j + 32hf + 16kt + r.
-  auto mask_max = [&](const acc_t (&acc)[2], int j, f32x16 (&sc)[2]) -> float {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kt][r] = (float)acc[kt][r];
+  // Invisible keys to -inf, and the row max of the raw scores (both lane halves);
+  // key of sc[kt][r] is 64j + 8hf + key_off2(kt, r), or with the fp8 P.V
+  // 64j + 32hf + 16kt + r.
+  auto mask_max = [&](int j, f32x16 (&sc)[2]) -> float {
     if ((64 * j + 64 > N) || (p.causal && 64 * j + 63 > wrow0) || (wrow0 + 31 >= N)) {
       const int rel = lim - 64 * j - (PV8 ? 32 : 8) * hf;
 #pragma unroll
@@ -524,10 +534,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // loaded for the next two steps.  Word indices are clamped into the row.
   const int lw_last = (d.lstride >> 1) - 1;
   unsigned int lw = lst32[min(1, lw_last)];
-  acc_t acc_cur[2];
-  // scores of the current block, fp32 with invisible keys at -inf: two sets for the
-  // 16-bit P.V, so that the step of parity P reads one while it fills the other for
-  // the next block
+  // scores of the current block, fp32 with invisible keys at -inf: two sets, so that
+  // the step of parity P reads one while the next block's Q.K^T fills the other
   f32x16 scA[2], scB[2];
   float mraw_cur = kNegInf;
   float ks_cur = (QK8 && cnt > 0) ? kscale_at(j_cur) : 0.0f;
@@ -537,17 +545,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     dma_v(j_cur, s0);
     wait_vmem_all();
     __syncthreads();
-    qk(s0, acc_cur, no_cb);
-    mraw_cur = mask_max(acc_cur, j_cur, scA);
+    qk(s0, scA, no_cb);
+    mraw_cur = mask_max(j_cur, scA);
   }
 
   unsigned int lw_nxt = 0u;
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;        // it & 1
-    // this block's scores, and the next block's made in this step (the fp8 P.V makes
-    // them after its P.V, in place)
-    f32x16 (&sc_cur)[2] = (P && !PV8) ? scB : scA;
-    f32x16 (&sc_nxt)[2] = (P || PV8) ? scA : scB;
+    // this block's scores, and the next block's made in this step
+    f32x16 (&sc_cur)[2] = P ? scB : scA;
+    f32x16 (&sc_nxt)[2] = P ? scA : scB;
     std::integral_constant<int, P> sp;
     std::integral_constant<int, 1 - P> sq;
     const int j = j_cur;
@@ -565,7 +572,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     __syncthreads();     // ... and every wavefront's; K stage P and V stage 1-P are free
     if (it + 2 < cnt) dma_k(j_n2, sp);
     if (it + 1 < cnt) dma_v(j_n1, sq);
-    float bias = 0.0f;   // int8 path: c * (q . kbar_j) for this lane's query
+    float bias = 0.0f;   // int8 path: c (q . kbar_j) for this lane's query, less the biased zero
     float slope_i8 = 0.0f;
     if constexpr (QK8) {
       unsigned short* kbh = (unsigned short*)Aux;            // [32][KBSTR] hi
@@ -607,22 +614,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       }
       bias = p.c * cw[(it & 31) * 33 + ql];
       // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
-      // that masked (-inf) scores stay -inf
-      slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f);
+      // that masked (-inf) scores stay -inf.  Per unit of the biased score the slope
+      // is 2^26 times that of s, and the offset takes away kScoreC0 times it.
+      slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f) * kScoreUnit;
+      bias = __builtin_fmaf(-slope_i8, kScoreC0, bias);
     }
     // The next block's Q.K^T (in a row's last step this multiplies whatever K stage
     // 1-P holds; the result is converted but never used).  With the 16-bit P.V it is
     // issued below, interleaved with this block's first P fragment.
-    acc_t acc_nxt[2];
-    if constexpr (PV8) qk(sq, acc_nxt, no_cb);
-    // 16-bit P.V: the next block's scores are converted (and their raw max taken) in
-    // quarters between the P.V MFMAs, in the same basic block, so that this work
-    // overlaps the MFMAs; masking, when the block needs it, follows the P.V
+    if constexpr (PV8) qk(sq, sc_nxt, no_cb);
+    // 16-bit P.V: the raw max of the next block's scores is taken in quarters between
+    // the P.V MFMAs, in the same basic block, so that this work overlaps the MFMAs;
+    // masking, when the block needs it, follows the P.V
     float mr_nxt = kNegInf;
-    auto conv_quarter = [&](auto qc) {
+    auto max_quarter = [&](auto qc) {
       constexpr int q = decltype(qc)::value, kt = q >> 1, r0 = 8 * (q & 1);
-#pragma unroll
-      for (int r = r0; r < r0 + 8; ++r) sc_nxt[kt][r] = (float)acc_nxt[kt][r];
 #pragma unroll
       for (int r = r0; r < r0 + 8; r += 2) mr_nxt = max3f(mr_nxt, sc_nxt[kt][r], sc_nxt[kt][r + 1]);
     };
@@ -721,8 +727,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         };
         auto make_pw = [&](auto kc) { static_for<0, 4>([&](auto wc) { make_pw_word(kc, wc); }); };
         // words of the first P fragment after each k-step of the next block's Q.K^T
-        qk(sq, acc_nxt, [&](auto sc) {
-          constexpr int s = decltype(sc)::value;
+        qk(sq, sc_nxt, [&](auto stc) {
+          constexpr int s = decltype(stc)::value;
           static_for<0, 4>([&](auto wc) {
             constexpr int wd = decltype(wc)::value;
             if constexpr (wd * KSTEPS / 4 == s && (KSTEPS <= 4 || wd * KSTEPS % 4 == 0))
@@ -739,18 +745,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
           if constexpr (dt == 0 && sg + 1 < 4) make_pw(std::integral_constant<int, sg + 1>{});
-          if constexpr (u % (kNU / 4) == 1) conv_quarter(std::integral_constant<int, u / (kNU / 4)>{});
+          if constexpr (u % (kNU / 4) == 1) max_quarter(std::integral_constant<int, u / (kNU / 4)>{});
         });
       }
       }
     // the next block's scores: mask and max (fp8 P.V: all of it here, under the
     // MFMAs still in flight)
     if constexpr (PV8) {
-      if (it + 1 < cnt) mraw_cur = mask_max(acc_nxt, j_n1, sc_nxt);
+      if (it + 1 < cnt) mraw_cur = mask_max(j_n1, sc_nxt);
     } else {
       if (skip) {   // the P.V (and the Q.K^T and conversion issued inside it) did not run
-        qk(sq, acc_nxt, no_cb);
-        static_for<0, 4>(conv_quarter);
+        qk(sq, sc_nxt, no_cb);
+        static_for<0, 4>(max_quarter);
       }
       if (it + 1 < cnt) {
         if ((64 * j_n1 + 64 > N) || (p.causal && 64 * j_n1 + 63 > wrow0) || (wrow0 + 31 >= N)) {
