@@ -117,6 +117,18 @@ constexpr int kScoreBits = 0x3e22f983;
 constexpr float kScoreC0 = 0.15915493667125702f;   // the float with those bits
 constexpr float kScoreUnit = 67108864.0f;           // 2^26
 
+// The first k-step of the int8 Q.K^T: C is the inline constant itself, so no register
+// block has to be filled with it.  The compiler does not see an MFMA here, so the asm
+// carries the wait states it would otherwise insert: two after any VALU write of A or
+// B (A comes from LDS reads with an explicit wait, B is written before the loop).
+// D is read only by the next k-step's MFMA with C exactly overlapping it, which needs
+// none.
+__device__ __forceinline__ i32x16 mfma_i8_first(i32x4 a, i32x4 b) {
+  i32x16 d;
+  asm("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, 0x3e22f983" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) unsigned char* lds_u8_ptr;
@@ -467,8 +479,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   auto qk = [&](auto kstage, f32x16 (&sc)[2], auto cb) {
     const unsigned int kb = (unsigned int)(size_t)(lds_u8_ptr)(decltype(kstage)::value ? Ks1 : Ks0);
     acc_t acc[2];
-    acc[0] = (acc_t)(QK8 ? kScoreBits : 0);
-    acc[1] = acc[0];
+    if constexpr (!QK8) {
+      acc[0] = (acc_t)(0);
+      acc[1] = acc[0];
+    }
     u32x4 kf[KSLOT][2];
     auto kissue = [&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -486,6 +500,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       for (int kt = 0; kt < 2; ++kt) {
         if constexpr (!QK8)
           acc[kt] = mma16<IN_F16>(__builtin_bit_cast(u16x8, kf[s % KSLOT][kt]), qf[s], acc[kt]);
+        else if constexpr (s == 0)
+          acc[kt] = mfma_i8_first(__builtin_bit_cast(i32x4, kf[s % KSLOT][kt]), q8[s]);
         else
           acc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kf[s % KSLOT][kt]),
                                                           q8[s], acc[kt], 0, 0, 0);
