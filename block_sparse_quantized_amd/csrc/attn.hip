@@ -79,6 +79,8 @@ __device__ __forceinline__ unsigned int pack2(float a, float b) {
   else return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // acc + (lo + hi) of a packed 16-bit pair, accumulated in fp32.
 template <bool F16>
 __device__ __forceinline__ float add_pair(unsigned int pr, float acc) {
@@ -87,6 +89,23 @@ __device__ __forceinline__ float add_pair(unsigned int pr, float acc) {
   else
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
                                            (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+
+// Row sums of a 16-bit P fragment on the MFMA.  Read as the B operand of a 16x16x32
+// MFMA, the 32x32x16 fragment (lane l: query l % 32, keys 8(l / 32) .. +7) puts, for
+// output column c, query c's and query c+16's keys in alternating groups of eight
+// (lanes c, c+16, c+32, c+48).  With A one on the groups of query c for output rows i
+// with (i / 4) even and on those of query c+16 for the others (sel), D[i][c], which
+// lane c + 16(i / 4) holds, is the fragment's sum for exactly that lane's own query
+// (l % 32), accumulated in fp32 from the rounded P that the P.V MFMAs multiply.
+template <bool F16>
+__device__ __forceinline__ f32x4 rowsum16(u16x8 sel, u16x8 pf, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sel), __builtin_bit_cast(f16x8, pf),
+                                                  c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sel),
+                                                   __builtin_bit_cast(bf16x8, pf), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -381,7 +400,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   float m_true = kNegInf;   // running row max of the visited blocks (filter)
   float m_ref = kNegInf;    // reference max of the exponentials
   float m_use = 0.0f;       // m_ref, or 0 while it is -inf
+  // 16-bit P.V after the int8 Q.K^T: row sums on the MFMA (rowsum16); element 0 holds
+  // this lane's query row sum (the other elements are not rescaled and not read).
+  // After the 16-bit Q.K^T (whose Q fragments take twice the registers) the extra
+  // registers would spill: there the sums are v_dot2 on the packed pairs (l_acc).
+  constexpr bool kSumMfma = QK8;
+  f32x4 lsum = (f32x4)(0.0f);
   float l_acc = 0.0f;       // this lane's partial row sum (its half of the keys)
+  const unsigned short one16 = PV_F16 ? 0x3c00 : 0x3f80;
+  const u16x8 lsel = (u16x8)((((lane >> 2) & 1) == ((lane >> 4) & 1)) ? one16 : (unsigned short)0);
   unsigned int n_skip = 0;
 
   // Direct-to-LDS loads of one block's K tile (into K stage KS) or V tile (into V
@@ -675,6 +702,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
         const float mu_new = (m_ref_new == kNegInf) ? 0.0f : m_ref_new;
         const float alpha = __builtin_amdgcn_exp2f(m_ref - mu_new);
         if constexpr (PV8) lacc[0] *= alpha;   // the only element read
+        else if constexpr (kSumMfma) lsum[0] *= alpha;   // the only element read
         else l_acc *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
@@ -738,7 +766,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r], slope, offs));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + 1], slope, offs));
           const unsigned int pr = pack2<PV_F16>(p0, p1);
-          l_acc = add_pair<PV_F16>(pr, l_acc);
+          if constexpr (!kSumMfma) l_acc = add_pair<PV_F16>(pr, l_acc);
           pw[k][decltype(wc)::value] = pr;
         };
         auto make_pw = [&](auto kc) { static_for<0, 4>([&](auto wc) { make_pw_word(kc, wc); }); };
@@ -760,6 +788,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           lds_wait<2 * later>(f0, f1);
           const u16x8 vf = __builtin_bit_cast(u16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[dt] = mma16<PV_F16>(vf, __builtin_bit_cast(u16x8, pw[sg]), oacc[dt]);
+          if constexpr (kSumMfma && dt == 1)
+            lsum = rowsum16<PV_F16>(lsel, __builtin_bit_cast(u16x8, pw[sg]), lsum);
           if constexpr (dt == 0 && sg + 1 < 4) make_pw(std::integral_constant<int, sg + 1>{});
           if constexpr (u % (kNU / 4) == 1) max_quarter(std::integral_constant<int, u / (kNU / 4)>{});
         });
@@ -801,7 +831,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   }
 
   // epilogue: O = acc / l, this lane's query row, columns 32dt + 8g + 4hf + 0..3
-  const float lt = PV8 ? lacc[0] : l_acc + partner32(l_acc, hf);
+  const float lt = PV8 ? lacc[0] : kSumMfma ? lsum[0] : l_acc + partner32(l_acc, hf);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     // fp8 P.V: the channel scales of the E4M3 V codes, all loaded before any store

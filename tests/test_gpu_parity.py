@@ -324,6 +324,39 @@ def test_int8_attention(dev, N, D, causal, pv16):
     assert sim_err < TOL16
 
 
+@pytest.mark.parametrize("D,qk8,pv", [(128, True, "fp16"), (64, True, "fp16"), (128, False, "bf16"),
+                                       (64, False, "bf16"), (64, False, "fp16"), (128, True, "fp8")])
+def test_rescale_per_row(dev, D, qk8, pv):
+    """Scores that grow along the keys at a different rate in every query row (and fall
+    in others), so that the reference max of the exponentials moves often, and at
+    different blocks for the rows of one wavefront: each row's O and row sum must be
+    rescaled by that row's own factor.  All blocks kept, filter off: dense attention."""
+    B, H, N = 1, 2, 2048
+    g = torch.Generator().manual_seed(21 + D)
+    q, k, v = (torch.randn(B, H, N, D, generator=g, dtype=torch.float64) for _ in range(3))
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    alpha = torch.rand(B, H, N, 1, generator=g, dtype=torch.float64) * 8.0 - 4.0
+    # +2 (log2 units) per 64 keys for a row with |alpha| = 4
+    kappa = 2.0 / (64 * 4 * math.log2(math.e) / math.sqrt(D))
+    t = kappa * torch.arange(N, dtype=torch.float64).view(1, 1, N, 1)
+    q, k = q + alpha * u, k + t * u
+    q, k, v = (x.to(torch.bfloat16).to(dev) for x in (q, k, v))
+    out = bsq.block_sparse_attn(q, k, v, None, qk_int8=qk8, pv_fp16=(pv == "fp16"),
+                                pv_fp8=(pv == "fp8"), filter_on=False)
+    torch.cuda.synchronize()
+    nQ, nK = so.num_blocks(N)
+    ones = np.ones((B, H, nQ, nK), dtype=bool)
+    exact, _ = oracle_outputs(q, k, v, ones, False)
+    err = np.abs(f64(out) - exact).max()
+    say(f"rescale per row D={D} int8={qk8} P.V {pv}: max abs err vs fp64 {err:.3e}")
+    if pv == "fp8":
+        ref = pv8_oracle(q, k, v, ones, False, None, "int8" if qk8 else "exact")
+        assert np.abs(f64(out) - ref).max() < TOLF8
+    else:
+        assert err < (TOL8 if qk8 else TOL16)
+
+
 # ------------------------------------------------------------------ fp8 P.V
 
 def pv8_oracle(q, k, v, mask, causal, lam, qk):
