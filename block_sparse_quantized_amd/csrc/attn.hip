@@ -243,6 +243,12 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float e) {
 __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// E4M3 16x16x128 with unit scales: the row sums of an fp8 P fragment, as rowsum16
+// does for 16-bit P (the 32x32x64 fragment puts query c's and c+16's keys in
+// alternating groups of 32 for output column c).
+__device__ __forceinline__ f32x4 rowsum_fp8(i32x8 sel, i32x8 pf, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf, c, 0, 0, 0, 127, 0, 127);
+}
 
 template <int D, bool IN_F16, bool PV_F16, bool QK8, bool PV8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims d) {
@@ -393,10 +399,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x16)(0.0f);
-  // fp8 P.V: the row sums come from one more MFMA with an all-ones A (E4M3 1.0 =
-  // 0x38), so they add exactly the rounded P that the P.V MFMAs see; every element
-  // of lacc then holds the lane's query-row sum over all 64 keys of each block.
-  f32x16 lacc = (f32x16)(0.0f);
+  // fp8 P.V: the row sums come from one more (16x16x128) MFMA whose A selects, with
+  // E4M3 ones (0x38), the key groups of each lane's own query, so they add exactly
+  // the rounded P that the P.V MFMAs see; element 0 of lacc then holds the lane's
+  // query-row sum over all 64 keys of each block.
+  f32x4 lacc = (f32x4)(0.0f);
   float m_true = kNegInf;   // running row max of the visited blocks (filter)
   float m_ref = kNegInf;    // reference max of the exponentials
   float m_use = 0.0f;       // m_ref, or 0 while it is -inf
@@ -730,8 +737,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           for (int x = 0; x < 4; ++x) e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[kt][r + x], slope, offs));
           pb[q] = pack_fp8x4(e[0], e[1], e[2], e[3]);
         }
-        const i32x8 ones = (i32x8)(0x38383838);
-        lacc = mma_fp8(ones, pb, lacc);
+        const i32x8 sel8 = (i32x8)((((lane >> 2) & 1) == ((lane >> 4) & 1)) ? 0x38383838 : 0);
+        lacc = rowsum_fp8(sel8, pb, lacc);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const i32x8 vf = __builtin_bit_cast(
