@@ -620,8 +620,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     const float ks_nxt = QK8 ? kscale_at(j_n1) : 0.0f;   // K step of the next block
     wait_vmem_all();     // this wavefront's DMAs of K(it+1) and V(it) have landed
     __syncthreads();     // ... and every wavefront's; K stage P and V stage 1-P are free
-    if (it + 2 < cnt) dma_k(j_n2, sp);
-    if (it + 1 < cnt) dma_v(j_n1, sq);
     float bias = 0.0f;   // int8 path: c (q . kbar_j) for this lane's query, less the biased zero
     float slope_i8 = 0.0f;
     if constexpr (QK8) {
@@ -629,25 +627,43 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       unsigned short* kbl = kbh + 32 * KBSTR;                // [32][KBSTR] lo
       float* cw = (float*)Aux + w * 32 * 33;                 // per wave [32][33]
       if ((it & 31) == 0) {
-        // kbar of the next 32 kept blocks as hi + lo in the input's 16-bit type,
-        // so that q . kbar runs on the MFMA at near-fp32 accuracy
-        for (int e = tid; e < 32 * (D / 4); e += 256) {
-          const int pr = e / (D / 4), c4 = (e % (D / 4)) * 4;
-          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (it + pr < cnt)
-            v = *(const float4*)(p.kbar + ((int64_t)bh * d.nK + list_at(it + pr)) * D + c4);
-          const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const unsigned short hi = f32_to_u16<IN_F16>(vv[q4]);
-            const unsigned short lo = f32_to_u16<IN_F16>(vv[q4] - u16_to_f32(hi, IN_F16));
-            kbh[pr * KBSTR + c4 + q4] = hi;
-            kbl[pr * KBSTR + c4 + q4] = lo;
-          }
-        }
-        __syncthreads();
+        // q . kbar_j of the next 32 kept blocks for this wave's queries, on the MFMA
+        // with kbar split into hi + lo halves of the input's 16-bit type (near-fp32
+        // accuracy).  The Q fragments are requested first, so that their latency
+        // overlaps the kbar loads.  Wave w converts kbar rows 8w .. 8w+7 (a block per
+        // row from a wave-uniform, scalar list read; two channels per lane).
         u16x8 qfr[KS16];
         load_qf(qfr);
+        constexpr int RPI = 128 / D;   // kbar rows per wave instruction
+        constexpr int NR = 8 / RPI;
+        const int rsub = lane / (D / 2), c2 = 2 * (lane % (D / 2));
+        // All loads are issued before any is used: the four list words holding this
+        // wave's eight entries (it is a multiple of 32, so they start at word
+        // it/2 + 4w; word indices clamped into the row), then the kbar rows (rows
+        // past the list's end read block 0 and are zeroed afterwards).
+        const int wb = (it >> 1) + 4 * w;
+        unsigned int lwv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lwv[q] = lst32[min(wb + q, lw_last)];
+        float2 kv[NR];
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+          const int idx = RPI * n + rsub, pr = 8 * w + idx;
+          const unsigned int wv = lwv[idx >> 1];
+          const int jb = (it + pr < cnt) ? (int)((idx & 1) ? (wv >> 16) : (wv & 0xffffu)) : 0;
+          kv[n] = *(const float2*)(p.kbar + ((int64_t)bh * d.nK + jb) * D + c2);
+        }
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+          const int pr = 8 * w + RPI * n + rsub;
+          const float2 v = (it + pr < cnt) ? kv[n] : make_float2(0.f, 0.f);
+          const unsigned int h0 = f32_to_u16<IN_F16>(v.x), h1 = f32_to_u16<IN_F16>(v.y);
+          const unsigned int l0 = f32_to_u16<IN_F16>(v.x - u16_to_f32((unsigned short)h0, IN_F16));
+          const unsigned int l1 = f32_to_u16<IN_F16>(v.y - u16_to_f32((unsigned short)h1, IN_F16));
+          *(unsigned int*)(kbh + pr * KBSTR + c2) = h0 | (h1 << 16);
+          *(unsigned int*)(kbl + pr * KBSTR + c2) = l0 | (l1 << 16);
+        }
+        __syncthreads();
         f32x16 cacc = (f32x16)(0.0f);
 #pragma unroll
         for (int s = 0; s < KS16; ++s) {
@@ -657,10 +673,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
           cacc = mma16<IN_F16>(al, qfr[s], cacc);
         }
         __syncthreads();  // every wave is done reading kbh/kbl, which cw overlays
-        // lane (hf, ql) holds C[block (r/4)*8 + 4hf + r%4][query ql]
+        // lane (hf, ql) holds C[block (r/4)*8 + 4hf + r%4][query ql].  A wave reads
+        // only its own cw rows, written by its own lanes, so no barrier follows: the
+        // next writes into this area come after the next step's barrier.
 #pragma unroll
         for (int r = 0; r < 16; ++r) cw[((r >> 2) * 8 + 4 * hf + (r & 3)) * 33 + ql] = cacc[r];
-        __syncthreads();
       }
       bias = p.c * cw[(it & 31) * 33 + ql];
       // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
@@ -669,6 +686,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f) * kScoreUnit;
       bias = __builtin_fmaf(-slope_i8, kScoreC0, bias);
     }
+    // DMAs of K(it+2) and V(it+1), after the int8 path's q . kbar pass, whose loads
+    // would otherwise wait for them as well
+    if (it + 2 < cnt) dma_k(j_n2, sp);
+    if (it + 1 < cnt) dma_v(j_n1, sq);
     // The next block's Q.K^T (in a row's last step this multiplies whatever K stage
     // 1-P holds; the result is converted but never used).  With the 16-bit P.V it is
     // issued below, interleaved with this block's first P fragment.
