@@ -28,6 +28,8 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
   w.kscale = take(BH * d.nK * sizeof(float));
   w.kbar = take(BH * d.nK * d.D * sizeof(float));
+  w.kc = take(BH * d.nK * 2 * d.D);
+  w.kcs = take(BH * sizeof(float));
   // fp32 inputs use 3 16-bit copies; fp8 P.V (16-bit inputs) its E4M3 V tiles
   const size_t conv16 = 3 * BH * (size_t)d.N * d.D * sizeof(uint16_t);
   const size_t vt8 = BH * (size_t)d.nK * 64 * d.D;
@@ -240,9 +242,13 @@ sparge_status run_attention(Ctx& c, const Operands& op, const sparge_tensor* out
     if (!k_ready)
       SPARGE_TRY(launch_quant_k(op.k, op.dtype16, c.d, k8, c.d.D, (int64_t)c.d.nK * 64 * c.d.D, ks,
                                 kb, c.s));
+    int8_t* kc = c.at<int8_t>(c.w.kc);
+    float* kcs = c.at<float>(c.w.kcs);
+    SPARGE_TRY(launch_kbar_codes(kb, c.d, kc, kcs, c.s));
     p.k8 = k8;
     p.kscale = ks;
-    p.kbar = kb;
+    p.kc = kc;
+    p.kcs = kcs;
   }
   if (o.prof_attn_begin) SPARGE_TRY(hipEventRecord((hipEvent_t)o.prof_attn_begin, c.s));
   SPARGE_TRY(launch_sparse_attn(p, c.d, c.s));

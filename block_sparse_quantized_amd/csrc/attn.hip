@@ -265,10 +265,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   constexpr int VCHUNK = VTILE / 1024;
   constexpr int kNU = 4 * DT;                 // (k-step, column tile) pairs of P.V
   constexpr int kVAhead = 4;                  // P.V pairs whose V reads run ahead
-  constexpr int KBSTR = D + 8;                // u16 per row of the kbar hi/lo tiles
-  constexpr int AUXB = QK8 ? ((2 * 32 * KBSTR * 2) > (4 * 32 * 33 * 4) ? (2 * 32 * KBSTR * 2)
-                                                                        : (4 * 32 * 33 * 4))
-                           : 16;
+  // int8 path: the q . kbar term from LDS only (see the pass in the step): this
+  // workgroup's Q residual codes per wave and k-step in the B-fragment order, two
+  // code rows of kbar for 16 kept blocks, and per wave q . kbar of those blocks
+  constexpr int R8B = QK8 ? 4 * KS8 * 64 * 16 : 16;
+  constexpr int KCB = QK8 ? 16 * 2 * D : 16;
+  constexpr int CWB = QK8 ? 4 * 16 * 32 * 4 : 16;
   // LDS tiles are written by direct-to-LDS loads (one 1 KB chunk per wavefront
   // instruction, lane-linear) and stored row-major with each row's 16-byte granules
   // XOR-swizzled by a function of the row (fk, fv), so fragment reads are free of
@@ -279,7 +281,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   __shared__ __attribute__((aligned(1024))) unsigned char Ks1[64 * KROW];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs0[VTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs1[VTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char Aux[AUXB];
+  __shared__ __attribute__((aligned(16))) unsigned char R8s[R8B];
+  __shared__ __attribute__((aligned(1024))) unsigned char KCs[KCB];
+  __shared__ __attribute__((aligned(16))) float CWs[CWB / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, hf = lane >> 5, ql = lane & 31;
@@ -306,9 +310,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   const int64_t ksrow = QK8 ? (int64_t)D : p.k.sN * 2;   // bytes between K rows in memory
   const int64_t vsrow = p.v.sN * 2;
 
-  // Q fragments in the B-operand layout: lane (hf, ql) holds Q[t][16s + 8hf .. +7].
-  // The int8 path needs them only for the q . kbar term every 32 blocks and
-  // reloads them there, to keep registers for the pipeline.
+  // Q fragments in the B-operand layout (16-bit Q.K^T): lane (hf, ql) holds
+  // Q[t][16s + 8hf .. +7].
   auto load_qf = [&](u16x8 (&f)[KS16]) {
 #pragma unroll
     for (int s = 0; s < KS16; ++s) {
@@ -322,6 +325,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // int8 Q codes: lane holds Q[t][32s + 16hf .. +15], one step per wavefront.
   i32x4 q8[QK8 ? KS8 : 1];
   float dq = 0.0f;
+  const float kc_step = QK8 ? p.kcs[bh] : 0.0f;   // step of this head's kbar codes
   if constexpr (QK8) {
     float vals[KS8][16];
     float amax = 0.0f;
@@ -342,19 +346,29 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
     dq = amax > 0.0f ? amax / 127.0f : 0.0f;
+    // and the residual codes of the q . kbar term: q ~= dq (code + r / 256) with
+    // r = clamp(rint((q / dq - code) * 256), -127, 127), kept in LDS (each lane reads
+    // back only what it wrote)
 #pragma unroll
     for (int s = 0; s < KS8; ++s) {
+      i32x4 r8w;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        unsigned int packed = 0;
+        unsigned int packed = 0, rpacked = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float c = __builtin_rintf(vals[s][4 * wd + e] * inv);
+          const float y = vals[s][4 * wd + e] * inv;
+          float c = __builtin_rintf(y);
           c = fminf(fmaxf(c, -127.0f), 127.0f);
           packed |= ((unsigned int)((int)c) & 0xffu) << (8 * e);
+          float r = __builtin_rintf((y - c) * 256.0f);
+          r = fminf(fmaxf(r, -127.0f), 127.0f);
+          rpacked |= ((unsigned int)((int)r) & 0xffu) << (8 * e);
         }
         q8[s][wd] = (int)packed;
+        r8w[wd] = (int)rpacked;
       }
+      *(i32x4*)(R8s + ((w * KS8 + s) * 64 + lane) * 16) = r8w;
     }
   }
 
@@ -583,6 +597,24 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // even step it, lw holds entries it+2 and it+3 and the word of it+4 and it+5 is
   // loaded for the next two steps.  Word indices are clamped into the row.
   const int lw_last = (d.lstride >> 1) - 1;
+  // int8 path: the two kbar code rows of kept blocks it1 .. it1+15 (it1 a multiple of
+  // 16) into KC, by direct-to-LDS loads (1 KB chunks, one per wavefront); each row's
+  // 16-byte granules XOR-swizzled by the row, so that the pass's fragment reads are
+  // free of bank conflicts.  Entries past the list's end load block 0.
+  auto dma_kc = [&](int it1) {
+    constexpr int RB = 2 * D, G = RB / 16, RPC = 1024 / RB, NCH = 16 * RB / 1024;
+    if (w < NCH) {
+      unsigned int lwv[RPC / 2];
+#pragma unroll
+      for (int q = 0; q < RPC / 2; ++q) lwv[q] = lst32[min((it1 >> 1) + (RPC * w) / 2 + q, lw_last)];
+      const int rr = lane / G, row = RPC * w + rr;
+      const unsigned int wv = lwv[rr >> 1];
+      const int jb = (it1 + row < cnt) ? (int)((rr & 1) ? (wv >> 16) : (wv & 0xffffu)) : 0;
+      const int lg = (lane % G) ^ (row & (G - 1));
+      __builtin_amdgcn_global_load_lds((const void*)(p.kc + ((int64_t)bh * d.nK + jb) * RB + 16 * lg),
+                                       (lds_void_ptr)(KCs + 1024 * w), 16, 0, 0);
+    }
+  };
   unsigned int lw = lst32[min(1, lw_last)];
   // scores of the current block, fp32 with invisible keys at -inf: two sets, so that
   // the step of parity P reads one while the next block's Q.K^T fills the other
@@ -593,6 +625,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     dma_k(j_cur, s0);
     if (cnt > 1) dma_k(j_n1, s1);
     dma_v(j_cur, s0);
+    if constexpr (QK8) dma_kc(0);
     wait_vmem_all();
     __syncthreads();
     qk(s0, scA, no_cb);
@@ -623,73 +656,51 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
     float bias = 0.0f;   // int8 path: c (q . kbar_j) for this lane's query, less the biased zero
     float slope_i8 = 0.0f;
     if constexpr (QK8) {
-      unsigned short* kbh = (unsigned short*)Aux;            // [32][KBSTR] hi
-      unsigned short* kbl = kbh + 32 * KBSTR;                // [32][KBSTR] lo
-      float* cw = (float*)Aux + w * 32 * 33;                 // per wave [32][33]
-      if ((it & 31) == 0) {
-        // q . kbar_j of the next 32 kept blocks for this wave's queries, on the MFMA
-        // with kbar split into hi + lo halves of the input's 16-bit type (near-fp32
-        // accuracy).  The Q fragments are requested first, so that their latency
-        // overlaps the kbar loads.  Wave w converts kbar rows 8w .. 8w+7 (a block per
-        // row from a wave-uniform, scalar list read; two channels per lane).
-        u16x8 qfr[KS16];
-        load_qf(qfr);
-        constexpr int RPI = 128 / D;   // kbar rows per wave instruction
-        constexpr int NR = 8 / RPI;
-        const int rsub = lane / (D / 2), c2 = 2 * (lane % (D / 2));
-        // All loads are issued before any is used: the four list words holding this
-        // wave's eight entries (it is a multiple of 32, so they start at word
-        // it/2 + 4w; word indices clamped into the row), then the kbar rows (rows
-        // past the list's end read block 0 and are zeroed afterwards).
-        const int wb = (it >> 1) + 4 * w;
-        unsigned int lwv[4];
+      float* cw = CWs + w * 16 * 32;   // per wave [16 blocks][32 queries]
+      if ((it & 15) == 0) {
+        // q . kbar_j of the next 16 kept blocks for this wave's queries, in integers
+        // on the int8 MFMA: with q ~= dq (q8 + r8 / 256) and kbar ~= sk (c1 + c2 / 256)
+        // (each second level within 1/512 of its first level's step),
+        // q . kbar ~= dq sk (q8 . c1 + (q8 . c2 + r8 . c1) / 256), leaving out the
+        // r8 . c2 term (2^-16 of the product's scale).  The codes of these blocks
+        // were staged in KC a step ahead; rows 16..31 of the A operand repeat rows
+        // 0..15 and their results are not used.  Everything a wave reads here is in
+        // LDS and either shared read-only or its own, so no barrier is needed.
+        constexpr int G = 2 * D / 16;   // 16-byte granules per code row
+        const int krow = ql & 15;
+        const unsigned char* kr = KCs + krow * 2 * D;
+        i32x16 p1 = (i32x16)(0), p2 = (i32x16)(0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lwv[q] = lst32[min(wb + q, lw_last)];
-        float2 kv[NR];
-#pragma unroll
-        for (int n = 0; n < NR; ++n) {
-          const int idx = RPI * n + rsub, pr = 8 * w + idx;
-          const unsigned int wv = lwv[idx >> 1];
-          const int jb = (it + pr < cnt) ? (int)((idx & 1) ? (wv >> 16) : (wv & 0xffffu)) : 0;
-          kv[n] = *(const float2*)(p.kbar + ((int64_t)bh * d.nK + jb) * D + c2);
+        for (int s = 0; s < KS8; ++s) {
+          const i32x4 a1 = *(const i32x4*)(kr + 16 * ((2 * s + hf) ^ (krow & (G - 1))));
+          const i32x4 a2 = *(const i32x4*)(kr + 16 * ((G / 2 + 2 * s + hf) ^ (krow & (G - 1))));
+          const i32x4 r8 = *(const i32x4*)(R8s + ((w * KS8 + s) * 64 + lane) * 16);
+          p1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, q8[s], p1, 0, 0, 0);
+          p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2, q8[s], p2, 0, 0, 0);
+          p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, r8, p2, 0, 0, 0);
         }
+        // lane (hf, ql) holds the result of block (r/4)*8 + 4hf + r%4 and query ql;
+        // blocks 0..15 are r < 8
+        const float sc = dq * kc_step;
 #pragma unroll
-        for (int n = 0; n < NR; ++n) {
-          const int pr = 8 * w + RPI * n + rsub;
-          const float2 v = (it + pr < cnt) ? kv[n] : make_float2(0.f, 0.f);
-          const unsigned int h0 = f32_to_u16<IN_F16>(v.x), h1 = f32_to_u16<IN_F16>(v.y);
-          const unsigned int l0 = f32_to_u16<IN_F16>(v.x - u16_to_f32((unsigned short)h0, IN_F16));
-          const unsigned int l1 = f32_to_u16<IN_F16>(v.y - u16_to_f32((unsigned short)h1, IN_F16));
-          *(unsigned int*)(kbh + pr * KBSTR + c2) = h0 | (h1 << 16);
-          *(unsigned int*)(kbl + pr * KBSTR + c2) = l0 | (l1 << 16);
-        }
-        __syncthreads();
-        f32x16 cacc = (f32x16)(0.0f);
-#pragma unroll
-        for (int s = 0; s < KS16; ++s) {
-          const u16x8 ah = *(const u16x8*)(kbh + ql * KBSTR + 16 * s + 8 * hf);
-          const u16x8 al = *(const u16x8*)(kbl + ql * KBSTR + 16 * s + 8 * hf);
-          cacc = mma16<IN_F16>(ah, qfr[s], cacc);
-          cacc = mma16<IN_F16>(al, qfr[s], cacc);
-        }
-        __syncthreads();  // every wave is done reading kbh/kbl, which cw overlays
-        // lane (hf, ql) holds C[block (r/4)*8 + 4hf + r%4][query ql].  A wave reads
-        // only its own cw rows, written by its own lanes, so no barrier follows: the
-        // next writes into this area come after the next step's barrier.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cw[((r >> 2) * 8 + 4 * hf + (r & 3)) * 33 + ql] = cacc[r];
+        for (int r = 0; r < 8; ++r)
+          cw[((r >> 2) * 8 + 4 * hf + (r & 3)) * 32 + ql] = sc * __builtin_fmaf((float)p2[r], 0.00390625f, (float)p1[r]);
       }
-      bias = p.c * cw[(it & 31) * 33 + ql];
+      bias = p.c * cw[(it & 15) * 32 + ql];
       // dq * dk can be 0 (an all-zero group or block); keep the slope positive so
       // that masked (-inf) scores stay -inf.  Per unit of the biased score the slope
       // is 2^26 times that of s, and the offset takes away kScoreC0 times it.
       slope_i8 = fmaxf(p.c * dq * ks_cur, 1e-30f) * kScoreUnit;
       bias = __builtin_fmaf(-slope_i8, kScoreC0, bias);
     }
-    // DMAs of K(it+2) and V(it+1), after the int8 path's q . kbar pass, whose loads
-    // would otherwise wait for them as well
+    // DMAs of K(it+2) and V(it+1), and before a q . kbar pass the next 16 blocks'
+    // kbar codes (the pass 15 steps ago has read KC, and every wavefront has passed
+    // a barrier since)
     if (it + 2 < cnt) dma_k(j_n2, sp);
     if (it + 1 < cnt) dma_v(j_n1, sq);
+    if constexpr (QK8) {
+      if ((it & 15) == 15 && it + 1 < cnt) dma_kc(it + 1);
+    }
     // The next block's Q.K^T (in a row's last step this multiplies whatever K stage
     // 1-P holds; the result is converted but never used).  With the 16-bit P.V it is
     // issued below, interleaved with this block's first P fragment.

@@ -153,7 +153,58 @@ __global__ __launch_bounds__(256) void reorder_kernel(View x, void* y, int64_t y
   *(uint4*)(yd + 16 * c) = *(const uint4*)(xs + 16 * c);
 }
 
+// Two-level int8 codes of the block means, for the q . kbar term of the int8
+// Q K^T on the int8 MFMA: one workgroup per (b, h); a = max_j,c |kbar_j[c]|,
+// step a / 127 (0 when a = 0), and per element, with y = kbar * (127 / a),
+// c1 = clamp(rint(y), +-127) and c2 = clamp(rint((y - c1) * 256), +-127), so that
+// kbar ~= step (c1 + c2 / 256) within step / 512.
+template <int D>
+__global__ __launch_bounds__(1024) void kbar_codes_kernel(const float* kbar, Dims d, int8_t* kc,
+                                                          float* kcs) {
+  const int bh = blockIdx.x;
+  const int64_t n = (int64_t)d.nK * D;
+  const float* src = kbar + (int64_t)bh * n;
+  float m = 0.0f;
+  for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * 1024) {
+    const float4 v = *(const float4*)(src + e);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  m = wave_max_f32(m);
+  __shared__ float wm[16];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, wm[i]);
+  const float inv = m > 0.0f ? 127.0f / m : 0.0f;
+  if (threadIdx.x == 0) kcs[bh] = m > 0.0f ? m / 127.0f : 0.0f;
+  int8_t* dst = kc + (int64_t)bh * n * 2;
+  for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * 1024) {
+    const float4 v = *(const float4*)(src + e);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    unsigned int w1 = 0, w2 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = x[i] * inv;
+      const float c1 = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+      const float c2 = fminf(fmaxf(__builtin_rintf((y - c1) * 256.0f), -127.0f), 127.0f);
+      w1 |= ((unsigned int)(int)c1 & 0xffu) << (8 * i);
+      w2 |= ((unsigned int)(int)c2 & 0xffu) << (8 * i);
+    }
+    const int64_t j = e / D, c = e % D;
+    *(unsigned int*)(dst + j * 2 * D + c) = w1;
+    *(unsigned int*)(dst + j * 2 * D + D + c) = w2;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kbar_codes(const float* kbar, const Dims& d, int8_t* kc, float* kcs, hipStream_t s) {
+  const dim3 grid((unsigned)(d.B * d.H));
+  if (d.D == 64) kbar_codes_kernel<64><<<grid, 1024, 0, s>>>(kbar, d, kc, kcs);
+  else kbar_codes_kernel<128><<<grid, 1024, 0, s>>>(kbar, d, kc, kcs);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes,
                           int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,

@@ -56,6 +56,7 @@ struct Workspace {
   size_t scores;                   // fp64 pooled scores (BH, nQ, nK)
   size_t lists, counts;            // uint16 kept-block lists (BH, nQ, lstride), int32 counts
   size_t k8, kscale, kbar;         // int8 K codes (BH, nK*64, D), fp32 steps, fp32 block means
+  size_t kc, kcs;                  // two-level int8 codes of the block means (BH, nK, 2D), steps (BH)
   size_t conv;                     // 16-bit copies of q, k (fp32 inputs) and v (3 x BH*N*D);
                                    // with fp8 P.V (16-bit inputs only) the E4M3 V tiles
   size_t vmaxp, vscale, vinv;      // fp8 P.V: per-block channel max |v| (BH, nQ, D), fp32
@@ -111,6 +112,10 @@ hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes
                           int64_t codes_row_stride, int64_t codes_head_stride, float* kscale,
                           float* kbar, hipStream_t s);
 
+// int8 Q K^T: per (b, h) a step sk = max |kbar| / 127 and two codes per element of
+// the block means, kbar ~= sk (c1 + c2 / 256): rows (BH, nK, 2D), c1 then c2.
+hipError_t launch_kbar_codes(const float* kbar, const Dims& d, int8_t* kc, float* kcs, hipStream_t s);
+
 // Fused pass over 16-bit Q, K, V (one workgroup per Q block): the block means and
 // self-similarities of launch_block_stats, plus, when codes != nullptr, the
 // block-smoothed int8 K of launch_quant_k (codes with D bytes per row, rows below
@@ -146,7 +151,8 @@ struct AttnParams {
   const int* counts;
   const int8_t* k8;      // int8 path: codes, (BH, nK*64, D)
   const float* kscale;   // (BH, nK)
-  const float* kbar;     // (BH, nK, D)
+  const int8_t* kc;      // two-level codes of the block means, (BH, nK, 2D)
+  const float* kcs;      // their step per head, (BH)
   const double* head_lambda; // nullable (H): per-head filter lambda (natural-log units)
   const unsigned char* v8t;  // fp8 P.V: E4M3 V tiles (BH, nK, D, 64)
   const float* vscale;       // fp8 P.V: channel scales (BH, D)

@@ -27,6 +27,11 @@ pytestmark = pytest.mark.gpu
 TOL16 = 2e-2
 TOL8 = 5e-2
 TOLF8 = 2e-2     # fp8 P.V against the oracle's fp8 P.V simulation on the same logits
+# fp8 P.V after the int8 Q.K^T: the kernel's q . kbar term (two-level int8 codes, about
+# 2^-16 of |q| |kbar|) and the simulation's exact one can differ by ~1e-4 log2 units per
+# (row, block), and a shift that small moves the simulation itself by up to 0.031
+# through single E4M3 rounding flips of dominant P (tests/test_oracle_fp8_noise.py)
+TOLF8_I8 = 5e-2
 
 
 def say(*a):
@@ -352,7 +357,7 @@ def test_rescale_per_row(dev, D, qk8, pv):
     say(f"rescale per row D={D} int8={qk8} P.V {pv}: max abs err vs fp64 {err:.3e}")
     if pv == "fp8":
         ref = pv8_oracle(q, k, v, ones, False, None, "int8" if qk8 else "exact")
-        assert np.abs(f64(out) - ref).max() < TOLF8
+        assert np.abs(f64(out) - ref).max() < (TOLF8_I8 if qk8 else TOLF8)
     else:
         assert err < (TOL8 if qk8 else TOL16)
 
@@ -390,7 +395,7 @@ def test_fp8_pv_block_sparse_matches_oracle(dev, N, D, dtype, qk8, filt):
     exact, _ = oracle_outputs(q, k, v, mnp, False, lam=-10.0 if filt else None)
     err = np.abs(f64(out) - ref).max()
     say(f"  max abs err vs fp8 simulation {err:.3e}, vs fp64 {np.abs(f64(out) - exact).max():.3e}")
-    assert err < TOLF8
+    assert err < (TOLF8_I8 if qk8 else TOLF8)
     assert np.all(f64(out)[0, 0, :min(N, 128)] == 0)
 
 
@@ -433,7 +438,7 @@ def test_fp8_pv_topk(dev, N, D, causal, qk8):
     err = np.abs(f64(out) - ref)[rows].max()
     vmax = np.abs(f64(v)).max()
     say(f"fp8 P.V topk N={N} D={D} causal={causal} int8={qk8}: err {err:.3e} (max|v| {vmax:.2f})")
-    assert err < TOLF8 * max(1.0, vmax / 4)
+    assert err < (TOLF8_I8 if qk8 else TOLF8) * max(1.0, vmax / 4)
 
 
 @pytest.mark.parametrize("path", ["fp8_int8", "fp8_bf16", "cdf", "cdf_fp8_int8"])
