@@ -83,7 +83,8 @@ typedef struct {
   int32_t qk_int8;       /* 1: int8 Q K^T (SageAttention base, [topgit] "Key
                             features"): Q one scale per 32 rows, K mean-smoothed and
                             scaled per 64-row block, the block mean added back as
-                            an exact q.kbar term.  Default 0 (16-bit Q K^T). */
+                            a q.kbar term (computed to ~2^-16 of |q| |kbar| from
+                            two-level int8 codes).  Default 0 (16-bit Q K^T). */
   int32_t pv_fp16;       /* 1: P and V rounded to fp16 for P.V; 0: the input's
                             16-bit type (bfloat16 for fp32 inputs).  Default 0. */
   int32_t pv_fp8;        /* 1: P.V in OCP FP8 E4M3 (the 8-bit-float P.V of the
