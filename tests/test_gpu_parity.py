@@ -329,6 +329,26 @@ def test_int8_attention(dev, N, D, causal, pv16):
     assert sim_err < TOL16
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_int8_zero_means_and_rows(dev, D):
+    """int8 Q.K^T edge cases of the q . kbar term: a head whose K is all zero (every
+    block mean zero, so the per-head code step is 0), and in another head an all-zero
+    K block and all-zero Q rows (zero int8 steps); dense, filter off, against fp64."""
+    B, H, N = 1, 2, 300
+    q, k, v = rand_qkv(B, H, N, D, torch.bfloat16, dev, seed=77 + D)
+    k[0, 0] = 0
+    k[0, 1, 64:128] = 0
+    q[0, 1, 32:64] = 0
+    out = bsq.block_sparse_attn(q, k, v, None, qk_int8=True, pv_fp16=True, filter_on=False)
+    torch.cuda.synchronize()
+    nQ, nK = so.num_blocks(N)
+    ref, _ = oracle_outputs(q, k, v, np.ones((B, H, nQ, nK), dtype=bool), False)
+    err = np.abs(f64(out) - ref).max()
+    say(f"int8 zero means/rows D={D}: max abs err vs fp64 {err:.3e}")
+    assert np.all(np.isfinite(f64(out)))
+    assert err < TOL8
+
+
 @pytest.mark.parametrize("D,qk8,pv", [(128, True, "fp16"), (64, True, "fp16"), (128, False, "bf16"),
                                        (64, False, "bf16"), (64, False, "fp16"), (128, True, "fp8")])
 def test_rescale_per_row(dev, D, qk8, pv):
