@@ -330,6 +330,21 @@ def test_int8_attention(dev, N, D, causal, pv16):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_int8_attention_fp32_inputs(dev, D):
+    """fp32 inputs on the int8 path (K codes and block means from quant_k_kernel, the
+    q . kbar codes from those means), top-k mask and outputs against fp64."""
+    q, k, v = rand_qkv(1, 2, 700, D, torch.float32, dev, seed=5 + D)
+    out, gm = bsq.sparge_topk_attn(q, k, v, 0.5, True, qk_int8=True, pv_fp16=True,
+                                   filter_on=False, return_mask=True)
+    torch.cuda.synchronize()
+    mask, rows = oracle_mask_and_rows(q, k, gm, 0.5, True)
+    ref, _ = oracle_outputs(q, k, v, mask, True)
+    err = np.abs(f64(out) - ref)[rows].max()
+    say(f"int8 fp32 inputs D={D}: max abs err vs fp64 {err:.3e}")
+    assert err < TOL8
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_int8_zero_means_and_rows(dev, D):
     """int8 Q.K^T edge cases of the q . kbar term: a head whose K is all zero (every
     block mean zero, so the per-head code step is 0), and in another head an all-zero
