@@ -493,16 +493,46 @@ sparge_status sparge_quantize_qk(const sparge_tensor* q, const sparge_tensor* k,
   if (!q_codes || !q_scales || !k_codes || !k_scales || !k_means) return SPARGE_E_NULL;
   Ctx c;
   if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
-  SPARGE_TRY(launch_quant_q(view_of(q), q->dtype, c.d, q_codes, q_scales, c.s));
-  if (k->dtype != SPARGE_F32) {
+  // the operands exactly as the attention path forms them: fp32 inputs rounded to
+  // bfloat16 first; Q's codes made by the attention kernel itself (codes-only launch);
+  // K's by the pass the attention path runs
+  View q16 = view_of(q), k16 = view_of(k);
+  int dtype16 = q->dtype, in_f16 = q->dtype == SPARGE_F16;
+  if (q->dtype == SPARGE_F32) {
+    const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
+    uint16_t* base = c.at<uint16_t>(c.w.conv);
+    const View packed{nullptr, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
+    SPARGE_TRY(launch_convert16(view_of(q), kF32, c.d, base, 0, c.s));
+    SPARGE_TRY(launch_convert16(view_of(k), kF32, c.d, base + one, 0, c.s));
+    q16 = packed;
+    q16.p = base;
+    k16 = packed;
+    k16.p = base + one;
+    dtype16 = kBF16;
+    in_f16 = 0;
+  }
+  AttnParams p{};
+  p.q = q16;
+  p.k = k16;
+  p.v = q16;
+  p.in_f16 = in_f16;
+  p.out_type = dtype16;
+  p.qk_int8 = 1;
+  p.pv_fp16 = 1;
+  p.kcs = c.at<float>(c.w.kcs);
+  p.q8_out = q_codes;
+  p.q8_scale_out = q_scales;
+  p.codes_only = 1;
+  SPARGE_TRY(launch_sparse_attn(p, c.d, c.s));
+  if (q->dtype != SPARGE_F32) {
     // the fused pass the attention path uses (its block statistics go unused)
-    SPARGE_TRY(launch_prep(view_of(q), view_of(k), view_of(k), k->dtype, c.d, c.at<double>(c.w.qmean),
+    SPARGE_TRY(launch_prep(q16, k16, k16, dtype16, c.d, c.at<double>(c.w.qmean),
                            c.at<double>(c.w.qsim), c.at<double>(c.w.kmean), c.at<double>(c.w.ksim),
                            k_codes, (int64_t)c.d.N * c.d.D, c.d.N, k_scales, k_means, nullptr,
                            nullptr, c.s));
   } else {
-    SPARGE_TRY(launch_quant_k(view_of(k), k->dtype, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D,
-                              k_scales, k_means, c.s));
+    SPARGE_TRY(launch_quant_k(k16, dtype16, c.d, k_codes, c.d.D, (int64_t)c.d.N * c.d.D, k_scales,
+                              k_means, c.s));
   }
   return SPARGE_OK;
 }

@@ -370,6 +370,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       }
       *(i32x4*)(R8s + ((w * KS8 + s) * 64 + lane) * 16) = r8w;
     }
+    // the codes as multiplied, for inspection: lane (hf, ql) holds row t, columns
+    // 32s + 16hf .. +15 of every k-step s
+    if (p.q8_out) {
+      if (row_ok) {
+        int8_t* dst = p.q8_out + ((int64_t)bh * N + t) * D + 16 * hf;
+#pragma unroll
+        for (int s = 0; s < KS8; ++s) *(i32x4*)(dst + 32 * s) = q8[s];
+      }
+      if (lane == 0 && wrow0 < N) p.q8_scale_out[(int64_t)bh * ((N + 31) / 32) + (wrow0 >> 5)] = dq;
+      if (p.codes_only) return;
+    }
   }
 
   const int cnt = p.counts[bh * d.nQ + i];

@@ -4,7 +4,8 @@
 // [topgit] "Key features"; [readme] "Avalible API").  Spec, all in IEEE fp32:
 //   K: per 64-row block, kbar_j = fp32(fp64 row sum / rows); k'' = fp32(k) - kbar_j;
 //      a = max|k''|; codes = clamp(rint(k'' * (127 / a)), -127, 127); step a / 127;
-//   Q: per 32-row group, a = max|q|, the same rounding, step a / 127.
+//   Q: per 32-row group, a = max|q|, the same rounding, step a / 127 (made by the
+//      attention kernel itself, in registers).
 // Every quantity that decides an integer code is computed in the same precision
 // and order as the reference steps: fp64 sums, IEEE fp32 division, subtraction,
 // product and round-half-to-even.
@@ -96,35 +97,6 @@ __global__ __launch_bounds__(256) void quant_k_kernel(View k, Dims d, int8_t* co
   float* mb = kbar + ((int64_t)bh * d.nK + j) * D;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) mb[CPL * lane + c] = mean[c];
-}
-
-// One wavefront per (b, h, 32-row Q group).
-template <int DT, int D>
-__global__ __launch_bounds__(256) void quant_q_kernel(View q, Dims d, int8_t* codes, float* qscale) {
-  constexpr int CPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int nG = (d.N + kQGroup - 1) / kQGroup;
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (int64_t)d.B * d.H * nG) return;
-  const int bh = (int)(task / nG), g = (int)(task % nG);
-  const int b = bh / d.H, h = bh % d.H;
-  const int r0 = g * kQGroup, n = min(kQGroup, d.N - r0);
-  const int64_t base = (int64_t)b * q.sB + (int64_t)h * q.sH + (int64_t)r0 * q.sN;
-  float a = 0.0f;
-  for (int r = 0; r < n; ++r)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      a = fmaxf(a, fabsf(ldf<DT>(q.p, base + (int64_t)r * q.sN + CPL * lane + c)));
-  a = wave_max_f32(a);
-  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-  int8_t* cb = codes + ((int64_t)bh * d.N + r0) * D;
-  for (int r = 0; r < n; ++r)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float x = ldf<DT>(q.p, base + (int64_t)r * q.sN + CPL * lane + c);
-      cb[(int64_t)r * D + CPL * lane + c] = a > 0.0f ? quant_code(x, inv) : (signed char)0;
-    }
-  if (lane == 0) qscale[(int64_t)bh * nG + g] = a > 0.0f ? a / 127.0f : 0.0f;
 }
 
 // One thread per 16-byte chunk of an output row.
@@ -225,25 +197,6 @@ hipError_t launch_quant_k(const View& k, int dtype, const Dims& d, int8_t* codes
     else SPARGE_QK(kBF16, 128);
   }
 #undef SPARGE_QK
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
-                          hipStream_t s) {
-  const int nG = (d.N + kQGroup - 1) / kQGroup;
-  const int64_t tasks = (int64_t)d.B * d.H * nG;
-  const dim3 grid((unsigned)((tasks + 3) / 4));
-#define SPARGE_QQ(DTV, DV) quant_q_kernel<DTV, DV><<<grid, 256, 0, s>>>(q, d, codes, qscale)
-  if (d.D == 64) {
-    if (dtype == kF32) SPARGE_QQ(kF32, 64);
-    else if (dtype == kF16) SPARGE_QQ(kF16, 64);
-    else SPARGE_QQ(kBF16, 64);
-  } else {
-    if (dtype == kF32) SPARGE_QQ(kF32, 128);
-    else if (dtype == kF16) SPARGE_QQ(kF16, 128);
-    else SPARGE_QQ(kBF16, 128);
-  }
-#undef SPARGE_QQ
   return hipGetLastError();
 }
 

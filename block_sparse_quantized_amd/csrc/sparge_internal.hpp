@@ -133,10 +133,6 @@ hipError_t launch_prep(const View& q, const View& k, const View& v, int dtype, c
 hipError_t launch_vt8(const View& v, int dtype, const Dims& d, const float* vmaxp, float* vscale,
                       float* vinv, unsigned char* vt, hipStream_t s);
 
-// int8 Q codes with one step per 32 rows (the kernel the attention kernel mirrors).
-hipError_t launch_quant_q(const View& q, int dtype, const Dims& d, int8_t* codes, float* qscale,
-                          hipStream_t s);
-
 struct AttnParams {
   View q, k;             // 16-bit (bf16 or fp16) views of Q and K
   View v;                // V in the P.V type (fp16 when pv_fp16, else Q's type)
@@ -157,6 +153,12 @@ struct AttnParams {
   const unsigned char* v8t;  // fp8 P.V: E4M3 V tiles (BH, nK, D, 64)
   const float* vscale;       // fp8 P.V: channel scales (BH, D)
   unsigned long long* counters;  // nullable: [2] = group updates, [3] = skipped updates
+  // int8 Q.K^T: when q8_out is set, every wavefront also writes the int8 Q codes it
+  // multiplies, (BH, N, D), and their step, (BH, ceil(N/32)); with codes_only it
+  // returns right after (no attention: lists, counts, K, V and O are not touched)
+  int8_t* q8_out;
+  float* q8_scale_out;
+  int codes_only;
 };
 
 hipError_t launch_sparse_attn(const AttnParams& p, const Dims& d, hipStream_t s);

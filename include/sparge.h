@@ -174,7 +174,12 @@ sparge_status sparge_predict_mask(const sparge_tensor* q, const sparge_tensor* k
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* The int8 operands of the qk_int8 option, for inspection (SageAttention base,
- * [topgit] "Key features").  All outputs device, contiguous:
+ * [topgit] "Key features"), exactly as the attention path forms them: the Q codes
+ * are written by the attention kernel itself (a launch that quantizes Q in
+ * registers as it does before its Q.K^T and then stops), the K codes by the pass
+ * the attention path runs.  fp32 inputs are first rounded to bfloat16, as for the
+ * attention products, so their codes are those of the rounded values.  All outputs
+ * device, contiguous:
  *   q_codes  int8  (B, H, N, D)       codes of Q, one scale per 32 rows
  *   q_scales float (B, H, ceil(N/32)) fp32 step max|q|/127 of each 32-row group
  *   k_codes  int8  (B, H, N, D)       codes of K - kbar_j (block-smoothed)

@@ -42,9 +42,6 @@ hipError_t launch_vt8(const View&, int, const Dims&, const float*, float*, float
                       hipStream_t) {
   return hipErrorNotSupported;
 }
-hipError_t launch_quant_q(const View&, int, const Dims&, int8_t*, float*, hipStream_t) {
-  return hipErrorNotSupported;
-}
 hipError_t launch_sparse_attn(const AttnParams&, const Dims&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_reorder(const View&, void*, int64_t, int64_t, int64_t, int, const Dims&, const int32_t*,
                           int64_t, int64_t, int, hipStream_t) {
