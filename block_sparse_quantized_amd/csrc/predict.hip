@@ -132,53 +132,56 @@ __global__ __launch_bounds__(256) void block_stats_kernel(View q, View k, Dims d
   if (lane == 0) (isq ? qsim : ksim)[(int64_t)bh * nb + blk] = sq / (double)(n * n);
 }
 
-// Pooled scores on the fp64 matrix cores (v_mfma_f64_16x16x4_f64): one 64 (i) x
-// 64 (j) tile per workgroup, a 32 x 32 quarter per wavefront as 2 x 2 MFMA tiles.
-// In the MFMA's operand layout lane (r, kq) = (lane % 16, lane / 16) supplies row
-// r of a 16-row tile at k = kq; at k-step s that is channel (D/4) kq + s, the same
-// channel for the Q and the K operand.  The means are stored in that order
-// (mean_index), so each 16-byte load of a wavefront (two k-steps of one 16-row
-// tile) is 1 KB of contiguous memory.  Every pair sums all D products in fp64;
-// only the association differs from a plain dot product.  Tiles and quarters
-// holding no valid pair under causality are skipped; tiles past the padded ends
-// re-read the last tile and rows and columns past the ends are not stored.
+// Pooled scores on the fp64 matrix cores (v_mfma_f64_16x16x4_f64): a wavefront
+// computes a 16T x 16T tile as T x T MFMA tiles, a workgroup's four wavefronts a
+// 32T x 32T one (T = 2 normally; T = 1 when that grid would leave most of the chip
+// idle, as for short sequences).  In the MFMA's operand layout lane (r, kq) =
+// (lane % 16, lane / 16) supplies row r of a 16-row tile at k = kq; at k-step s that
+// is channel (D/4) kq + s, the same channel for the Q and the K operand.  The means
+// are stored in that order (mean_index), so each 16-byte load of a wavefront (two
+// k-steps of one 16-row tile) is 1 KB of contiguous memory.  Every pair sums all D
+// products in fp64 in the same order for either T; only the association differs
+// from a plain dot product.  Tiles and wavefront tiles holding no valid pair under
+// causality are skipped; tiles past the padded ends re-read the last tile and rows
+// and columns past the ends are not stored.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <int D, int T>
 __global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qmean, const double* kmean,
                                                             Dims d, int causal, double scale,
                                                             double* scores) {
   constexpr int NP = D / 8;    // k-step pairs
   constexpr int CP = 4;        // pairs per chunk
-  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
-  if (causal && j0 > 2 * (i0 + 63) + 1) return;
+  constexpr int WT = 16 * T;   // wavefront tile side
+  const int j0 = blockIdx.x * 2 * WT, i0 = blockIdx.y * 2 * WT, bh = blockIdx.z;
+  if (causal && j0 > 2 * (i0 + 2 * WT - 1) + 1) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int iw = i0 + 32 * (w >> 1), jw = j0 + 32 * (w & 1);
+  const int iw = i0 + WT * (w >> 1), jw = j0 + WT * (w & 1);
   // no barriers below, so a wavefront with no valid pair may leave early
-  if (causal && jw > 2 * (iw + 31) + 1) return;
+  if (causal && jw > 2 * (iw + WT - 1) + 1) return;
   const int nQp = pad16(d.nQ), nKp = pad16(d.nK);
-  const double2* qa[2];
-  const double2* kb[2];
+  const double2* qa[T];
+  const double2* kb[T];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < T; ++t) {
     qa[t] = (const double2*)(qmean + ((int64_t)bh * nQp + min(iw + 16 * t, nQp - 16)) * D) + lane;
     kb[t] = (const double2*)(kmean + ((int64_t)bh * nKp + min(jw + 16 * t, nKp - 16)) * D) + lane;
   }
-  double2 a[2][2][CP], b[2][2][CP];   // [buffer][tile][pair]
+  double2 a[2][T][CP], b[2][T][CP];   // [buffer][tile][pair]
   auto load = [&](int buf, int p0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int e = 0; e < CP; ++e) {
         a[buf][t][e] = qa[t][64 * (p0 + e)];
         b[buf][t][e] = kb[t][64 * (p0 + e)];
       }
   };
-  f64x4 acc[2][2];
+  f64x4 acc[T][T];
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+  for (int ti = 0; ti < T; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = (f64x4)(0.0);
+    for (int tj = 0; tj < T; ++tj) acc[ti][tj] = (f64x4)(0.0);
   load(0, 0);
 #pragma unroll
   for (int c = 0; c < NP / CP; ++c) {
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qmean,
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
+        for (int ti = 0; ti < T; ++ti)
 #pragma unroll
-          for (int tj = 0; tj < 2; ++tj) {
+          for (int tj = 0; tj < T; ++tj) {
             const double av = half ? a[cur][ti][e].y : a[cur][ti][e].x;
             const double bv = half ? b[cur][tj][e].y : b[cur][tj][e].x;
             acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[ti][tj], 0, 0, 0);
@@ -200,9 +203,9 @@ __global__ __launch_bounds__(256) void pooled_scores_kernel(const double* qmean,
   // lane (r, kq) holds rows kq + 4e (e = 0..3) of column r of each output tile
   const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+  for (int ti = 0; ti < T; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj) {
+    for (int tj = 0; tj < T; ++tj) {
       const int j = jw + 16 * tj + r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -675,12 +678,21 @@ hipError_t launch_block_stats(const View& q, const View& k, int dtype, const Dim
 
 hipError_t launch_pooled_scores(const double* qmean, const double* kmean, const Dims& d, int causal,
                                 double scale, double* scores, hipStream_t s) {
-  const dim3 grid((unsigned)((d.nK + 63) / 64), (unsigned)((d.nQ + 63) / 64),
+  // 64 x 64 tiles per workgroup, or 32 x 32 when the larger tiles give under 1024
+  // workgroups (short sequences: more, shorter wavefronts fill more of the chip)
+  const int64_t big = (int64_t)((d.nK + 63) / 64) * ((d.nQ + 63) / 64) * d.B * d.H;
+  const int side = big < 1024 ? 32 : 64;
+  const dim3 grid((unsigned)((d.nK + side - 1) / side), (unsigned)((d.nQ + side - 1) / side),
                   (unsigned)(d.B * d.H));
-  if (d.D == 64)
-    pooled_scores_kernel<64><<<grid, 256, 0, s>>>(qmean, kmean, d, causal, scale, scores);
-  else
-    pooled_scores_kernel<128><<<grid, 256, 0, s>>>(qmean, kmean, d, causal, scale, scores);
+#define SPARGE_POOLED(DV, TV) pooled_scores_kernel<DV, TV><<<grid, 256, 0, s>>>(qmean, kmean, d, causal, scale, scores)
+  if (d.D == 64) {
+    if (side == 32) SPARGE_POOLED(64, 1);
+    else SPARGE_POOLED(64, 2);
+  } else {
+    if (side == 32) SPARGE_POOLED(128, 1);
+    else SPARGE_POOLED(128, 2);
+  }
+#undef SPARGE_POOLED
   return hipGetLastError();
 }
 

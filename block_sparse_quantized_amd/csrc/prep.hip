@@ -193,11 +193,28 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
     }
   };
   // Channel sums s and unit-row sums u of tile rows [lo, hi) for this thread's
-  // channel, in row order.
+  // channel, in row order.  Eight rows at a time: their LDS reads are all issued
+  // before the first sum needs one, so the pass waits for LDS once per eight rows.
   auto channel_pass = [&](int c, int lo, int hi, double& s, double& u) {
     s = 0.0;
     u = 0.0;
-    for (int r = lo; r < hi; ++r) {
+    int r = lo;
+    for (; r + 8 <= hi; r += 8) {
+      unsigned short xr[8];
+      double iv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xr[e] = *(const unsigned short*)(tile + (r + e) * ROWB + 2 * c);
+        iv[e] = inv_s[r + e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double x = u16_to_f32(xr[e], F16);
+        s = s + x;
+        u = fma(x, iv[e], u);
+      }
+    }
+    for (; r < hi; ++r) {
       const double x = u16_to_f32(*(const unsigned short*)(tile + r * ROWB + 2 * c), F16);
       s = s + x;
       u = fma(x, inv_s[r], u);
