@@ -84,7 +84,8 @@ def dense_equiv_ops(B, H, N, D, causal):
 class Path:
     """The hot path of one workload with preallocated outputs and workspace."""
 
-    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None, pv_fp8=None, cdf=None):
+    def __init__(self, wl, dev, qk_int8=None, pv_fp16=None, inputs=None, pv_fp8=None, cdf=None,
+                 filter_lambda=-10.0):
         import torch
 
         import block_sparse_quantized_amd as bsq
@@ -94,6 +95,7 @@ class Path:
         self.pv_fp16 = wl.pv_fp16 if pv_fp16 is None else pv_fp16
         self.pv_fp8 = wl.pv_fp8 if pv_fp8 is None else pv_fp8
         self.cdf = cdf   # softmax-mass threshold of the threshold selection, or None (top-k)
+        self.lam = filter_lambda
         t0 = time.time()
         if inputs is None:
             self.q, self.k, self.v = synth.make_qkv(wl, device=dev)
@@ -122,17 +124,17 @@ class Path:
             q, k, v, out = self.qr, self.kr, self.vr, self.orr
         if wl.api == "block_sparse":
             r = bsq.block_sparse_attn(q, k, v, self.mask, filter_on=wl.filter_on,
-                                      qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                      filter_lambda=self.lam, qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
                                       pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
                                       prof=prof)
         elif self.cdf is not None:
             r = bsq.sparge_cdf_attn(q, k, v, self.cdf, wl.causal, filter_on=wl.filter_on,
-                                    qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                    filter_lambda=self.lam, qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
                                     pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
                                     prof=prof)
         else:
             r = bsq.sparge_topk_attn(q, k, v, wl.topk, wl.causal, filter_on=wl.filter_on,
-                                     qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
+                                     filter_lambda=self.lam, qk_int8=self.qk_int8, pv_fp16=self.pv_fp16,
                                      pv_fp8=self.pv_fp8, stats=stats, out=out, workspace=self.ws,
                                      prof=prof)
         if wl.hilbert:
@@ -238,82 +240,152 @@ def committed_traffic(wl_name, kernel_src, dtype):
     return None
 
 
-def cpu_baseline(wl, q, k, v, budget_s=20.0):
-    """The CPU oracle (fp64 numpy) timed on a bounded sample of the workload."""
-    import numpy as np
+# ---- CPU baseline: the oracle in a pool of worker processes -------------------------
+# The workers are forked at start-up, before this process touches the GPU, and hold no
+# GPU state.  Each draws head (0, 0) of the workload on the CPU (the seeded generator's
+# CPU stream: the same recipe and shapes as the GPU draw), predicts its block mask with
+# the oracle once, and then computes the oracle's stage-2 output for the block rows it
+# is handed, one at a time, with BLAS held to one thread.
 
+_W = {}
+
+
+def _cpu_worker_init(name):
+    # one BLAS thread per worker: through the environment for a BLAS library loaded
+    # after this point, and through threadpoolctl for one already loaded
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    import torch
+    torch.set_num_threads(1)
+    from block_sparse_quantized_amd import synth
     from oracle import sparge_oracle as so
-    B, H, N, D = q.shape
-    qn = q[0, 0].double().cpu().numpy()
-    kn = k[0, 0].double().cpu().numpy()
-    vn = v[0, 0].double().cpu().numpy()
-    t0 = time.perf_counter()
-    c0 = time.process_time()   # CPU time of every thread of this process
+    wl = synth.workload(name, B=1, H=1)
+    q, k, v = (t[0, 0].double().numpy() for t in synth.make_qkv(wl, device="cpu"))
     if wl.api == "block_sparse":
-        from block_sparse_quantized_amd import synth
         mask = synth.make_block_mask(wl, device="cpu")[0, 0].numpy().astype(bool)
-        t_pred = 0.0
     else:
-        mask, _ = so.predict_mask(qn, kn, so.OracleParams(topk=wl.topk, causal=wl.causal))
-        t_pred = time.perf_counter() - t0
-    nQ = mask.shape[0]
+        mask, _ = so.predict_mask(q, k, so.OracleParams(topk=wl.topk, causal=wl.causal))
+    _W.update(wl=wl, q=q, k=k, v=v, mask=mask)
+
+
+def _cpu_worker_rows(i):
+    """The oracle's output for block row i of head (0, 0): (dense-equivalent ops, rows)."""
+    from oracle import sparge_oracle as so
+    wl, q, k, v, mask = _W["wl"], _W["q"], _W["k"], _W["v"], _W["mask"]
+    N, D = q.shape
     lam = -10.0 if wl.filter_on else None
-    # block rows visited in a fixed spread (longest first), until the budget is spent
+    groups = [(i, g) for g in range(4) if BQ * i + G * g < N]
+    so.attend_rows(q, k, v, mask, groups, wl.causal, lam=lam)
+    ops, rows = 0.0, 0
+    for (_, g) in groups:
+        r0 = BQ * i + G * g
+        r1 = min(N, r0 + G, BQ * i + BQ)
+        keys = (sum(range(r0 + 1, r1 + 1))) if wl.causal else (r1 - r0) * N
+        ops += 4.0 * D * keys
+        rows += r1 - r0
+    return ops, rows
+
+
+def cpu_pool(name, workers=None):
+    """The forked worker pool (call before any GPU work)."""
+    import multiprocessing
+    n = workers or min(16, len(os.sched_getaffinity(0)))
+    return multiprocessing.get_context("fork").Pool(n, initializer=_cpu_worker_init, initargs=(name,)), n
+
+
+def cpu_baseline(wl, pool, nworkers, budget_s=20.0):
+    """The CPU oracle (fp64 numpy) on a bounded sample of the workload: block rows of
+    head (0, 0), spread over the sequence (longest first), one per worker at a time,
+    handed out until the budget is spent."""
+    import multiprocessing  # noqa: F401
+    nQ = (wl.N + BQ - 1) // BQ
     order = []
     for stride in (max(1, nQ // 8), max(1, nQ // 64), 1):
         order += [i for i in range(nQ - 1, -1, -stride) if i not in order]
-    done_rows, dense_ops, t_attn = 0, 0.0, 0.0
-    groups = []
-    for i in order:
-        if time.perf_counter() - t0 > budget_s:
-            break
-        for g in range(4):
-            r0 = BQ * i + G * g
-            if r0 >= N:
-                continue
-            r1 = min(N, r0 + G, BQ * i + BQ)
-            t1 = time.perf_counter()
-            so.attend_rows(qn, kn, vn, mask, [(i, g)], wl.causal, lam=lam)
-            t_attn += time.perf_counter() - t1
-            rows = np.arange(r0, r1)
-            keys = (rows + 1) if wl.causal else np.full(rows.size, N)
-            dense_ops += float(4.0 * D * keys.sum())
-            done_rows += r1 - r0
-            groups.append((i, g))
-    t = t_attn + t_pred * done_rows / N
-    # cores actually used: CPU time over wall time of the sampled run (the oracle's
-    # small matrix products leave most of the BLAS threads idle)
-    cores = round((time.process_time() - c0) / max(1e-9, time.perf_counter() - t0), 1)
-    return {"value": round(dense_ops / t / 1e12, 8), "unit": "TOPS (dense-equivalent)",
-            "cores": cores, "kind": "oracle",
-            "sample": (f"head (0,0) of {wl.name}: full stage-1 oracle predictor ({t_pred:.2f}s, "
-                       f"pro-rated by rows) + stage-2 fp64 oracle attention"
-                       f"{' with the filter' if lam is not None else ''} for {len(groups)} "
-                       f"32-row groups ({done_rows} rows in {len(set(i for i, _ in groups))} block rows, "
-                       f"spread over the sequence, longest first); "
-                       f"value = dense-equivalent ops of those rows / time ({t:.2f}s); cores = CPU "
-                       f"time / wall time of the run, on a host with {len(os.sched_getaffinity(0))} "
-                       f"usable cores")}
+    # every worker has drawn its inputs and predicted its mask (its initializer, run
+    # at start-up while the GPU part ran) before the clock starts
+    warm = [pool.apply_async(os.getpid) for _ in range(4 * nworkers)]
+    [w.get() for w in warm]
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    pending, nxt, ops, rows, done_rows = [], 0, 0.0, 0, []
+    while nxt < len(order) and len(pending) < nworkers:
+        pending.append((order[nxt], pool.apply_async(_cpu_worker_rows, (order[nxt],))))
+        nxt += 1
+    while pending:
+        i, r = pending.pop(0)
+        o, n = r.get()
+        ops += o
+        rows += n
+        done_rows.append(i)
+        if nxt < len(order) and time.perf_counter() - t0 < budget_s:
+            pending.append((order[nxt], pool.apply_async(_cpu_worker_rows, (order[nxt],))))
+            nxt += 1
+    t = time.perf_counter() - t0
+    pool.close()
+    pool.join()
+    return {"value": round(ops / t / 1e12, 8), "unit": "TOPS (dense-equivalent)",
+            "cores": nworkers, "kind": "oracle",
+            "sample": (f"head (0,0) of {wl.name} drawn on the CPU: stage-2 fp64 oracle attention"
+                       f"{' with the filter' if wl.filter_on else ''} of {len(done_rows)} block rows "
+                       f"({rows} query rows, spread over the sequence, longest first) in {t:.2f}s, in "
+                       f"{nworkers} worker processes (one BLAS thread each, each having drawn the "
+                       f"head and predicted its mask with the oracle before the clock started); "
+                       f"value = dense-equivalent ops of those rows / wall time"),
+            "host": host_info()}
+
+
+def host_info():
+    """CPU model, usable cores, numpy and its BLAS."""
+    import numpy as np
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{d.get('internal_api')} {d.get('version')}" for d in threadpool_info()
+                if d.get("user_api") == "blas"]
+        blas = ", ".join(sorted(set(libs))) or blas
+    except Exception:
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas}
 
 
 def sdpa_baseline(q, k, v, causal, steps=3):
-    """torch SDPA (flash / memory-efficient only) in bf16 at the same shape."""
+    """torch SDPA in bf16 at the same shape, each fused backend on its own (flash, then
+    memory-efficient); returns {backend: ms per call} for those that run."""
     import torch
     import torch.nn.functional as F
+    res = {}
     try:
         from torch.nn.attention import SDPBackend, sdpa_kernel
-        qb, kb, vb = (t.to(torch.bfloat16) for t in (q, k, v))
-        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
-            F.scaled_dot_product_attention(qb, kb, vb, is_causal=causal)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(steps):
+    except Exception as e:
+        log(f"[bench] torch SDPA backends unavailable: {e}")
+        return res
+    qb, kb, vb = (t.to(torch.bfloat16) for t in (q, k, v))
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
                 F.scaled_dot_product_attention(qb, kb, vb, is_causal=causal)
-            torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
-    except Exception as e:  # no fused backend at this shape
-        log(f"[bench] torch SDPA baseline unavailable: {e}")
-        return None
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    F.scaled_dot_product_attention(qb, kb, vb, is_causal=causal)
+                torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) * 1e3 / steps
+        except Exception as e:  # this backend does not take the shape
+            log(f"[bench] torch SDPA {name} backend unavailable: {e}")
+    return res
 
 
 SWEEP_N = (8192, 16384, 32768, 65536, 131072)
@@ -380,11 +452,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from block_sparse_quantized_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    pool = None
+    if not args.no_cpu_baseline:
+        pool, nworkers = cpu_pool(wl.name)   # forked before anything touches the GPU
+
     import torch
 
-    from block_sparse_quantized_amd import synth
     dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
     ev = HipEvents()
     log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} N={wl.N} D={wl.D} steps={args.steps} "
         f"warmup={args.warmup}")
@@ -442,6 +518,22 @@ def main():
                 "tops_dense_equiv": round(dense / (sc * 1e-3) / 1e12, 2),
                 "kept_block_density": round(stc["kept_blocks"] / max(1, stc["valid_blocks"]), 4)}
             del pc
+        if wl.filter_on:
+            # what the softmax-aware filter buys on these inputs: the same step with the
+            # filter off and with looser thresholds (lambda in natural-log logit units)
+            fe = []
+            for lam in (None, -10.0, -6.0, -3.0):
+                wf = synth.workload(wl.name, filter_on=lam is not None)
+                pf = Path(wf, dev, qk_int8=path.qk_int8, pv_fp16=path.pv_fp16, pv_fp8=path.pv_fp8,
+                          inputs=(path.q, path.k, path.v, path.mask),
+                          filter_lambda=-10.0 if lam is None else lam)
+                _, stf = pf.step(stats=True)
+                sf, af, _ = time_path(pf, ev, max(3, args.steps // 2), 1)
+                fe.append({"filter_lambda": lam, "ms_per_step": round(sf, 4), "attention_ms": round(af, 4),
+                           "skipped_update_frac": round(stf["skipped_updates"] / max(1, stf["group_updates"]), 5)})
+                log(f"[bench] filter lambda={lam}: {sf:.3f} ms/step, skipped {fe[-1]['skipped_update_frac']}")
+                del pf
+            extras["filter_effect"] = fe
         if wl.api != "block_sparse" and not wl.hilbert:
             pd = Path(synth.workload(wl.name, topk=1.0, filter_on=False), dev, qk_int8=False,
                       pv_fp16=False, inputs=(path.q, path.k, path.v, path.mask))
@@ -451,14 +543,18 @@ def main():
             del pd
         if wl.name in ("llm8k", "llm128k"):
             extras["sweep"] = sweep(wl, dev, ev, path)
-        ms_sdpa = sdpa_baseline(path.q, path.k, path.v, wl.causal)
-        if ms_sdpa is not None:
-            extras["dense_torch_sdpa_bf16"] = {"ms_per_step": round(ms_sdpa, 3),
-                                              "tops_dense_equiv": round(dense / (ms_sdpa * 1e-3) / 1e12, 2)}
+        sd = sdpa_baseline(path.q, path.k, path.v, wl.causal)
+        if sd:
+            best = min(sd, key=sd.get)
+            extras["dense_torch_sdpa_bf16"] = {
+                "backend": best, "ms_per_step": round(sd[best], 3),
+                "tops_dense_equiv": round(dense / (sd[best] * 1e-3) / 1e12, 2),
+                "per_backend_ms": {b: round(t, 3) for b, t in sd.items()},
+                "torch": torch.__version__}
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(wl, path.q, path.k, path.v)
+        cpu = cpu_baseline(wl, pool, nworkers)
         log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
 
     density = stats["kept_blocks"] / max(1, stats["valid_blocks"])
