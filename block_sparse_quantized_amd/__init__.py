@@ -8,6 +8,7 @@ a GPU, the calls raise.
 
 Functions share the C names:
     sparge_topk_attn(q, k, v, topk=0.5, is_causal=False, ...)
+    sparge_topk_attn_noalloc(q, k, v, topk=0.5, is_causal=False, ...)
     sparge_cdf_attn(q, k, v, cdf_threshold, is_causal=False, ...)
     block_sparse_attn(q, k, v, mask_id=None, ...)
     sparge_predict_mask(q, k, topk, is_causal, ...)
@@ -39,6 +40,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "sparge_topk_attn",
+    "sparge_topk_attn_noalloc",
     "sparge_cdf_attn",
     "block_sparse_attn",
     "sparge_predict_mask",
@@ -181,6 +183,31 @@ def sparge_topk_attn(q, k, v, topk: float = 0.5, is_causal: bool = False, *, sca
                            scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16,
                            pv_fp8, return_mask, stats, out, workspace, prof, head_select,
                            head_sim_threshold, head_filter_lambda)
+
+
+def sparge_topk_attn_noalloc(q, k, v, topk: float = 0.5, is_causal: bool = False, *, scale=None,
+                             sim_threshold: float = 0.1, filter_lambda: float = -10.0,
+                             filter_on: bool = True, qk_int8: bool = False, pv_fp16: bool = False,
+                             pv_fp8: bool = False, return_mask: bool = False, stats: bool = False,
+                             out=None):
+    """``sparge_topk_attn`` on the library's own static device scratch (no workspace, no
+    allocation in the call: for graph capture and loops that may not allocate).  Calls
+    that overlap on one GPU race on that scratch; problems beyond it raise."""
+    if out is None:
+        out = torch.empty_like(q)
+    mask = torch.empty(_mask_shape(q), dtype=torch.uint8, device=q.device) if return_mask else None
+    o, st = _opts(scale, sim_threshold, filter_lambda, filter_on, qk_int8, pv_fp16, mask, stats,
+                  None, pv_fp8)
+    dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
+    _check(lib().sparge_topk_attn_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                          ctypes.byref(do), ctypes.c_double(topk), int(bool(is_causal)),
+                                          ctypes.byref(o), _stream(q)), "sparge_topk_attn_noalloc")
+    res = [out]
+    if return_mask:
+        res.append(mask)
+    if stats:
+        res.append(_stats_dict(st))
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def sparge_cdf_attn(q, k, v, cdf_threshold: float, is_causal: bool = False, *, scale=None,

@@ -58,6 +58,7 @@ PROTOTYPES = {
                                 ctypes.c_size_t, _vp]),
     "sparge_cdf_attn": (_i32, [_T, _T, _T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp,
                                ctypes.c_size_t, _vp]),
+    "sparge_topk_attn_noalloc": (_i32, [_T, _T, _T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp]),
     "block_sparse_attn": (_i32, [_T, _T, _T, _vp, _T, _P(SpargeOpts), _vp, ctypes.c_size_t, _vp]),
     "sparge_predict_mask": (_i32, [_T, _T, ctypes.c_double, _i32, _P(SpargeOpts), _vp, _vp,
                                    ctypes.c_size_t, _vp]),

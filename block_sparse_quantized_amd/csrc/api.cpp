@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/sparge.h"
@@ -13,9 +15,25 @@ namespace sparge {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Workspace plan_workspace(const Dims& d, int dtype) {
+Workspace plan_workspace(const Dims& d, int dtype, const PlanNeeds* need) {
   Workspace w{};
   const size_t BH = (size_t)d.B * d.H;
+  const size_t one16 = BH * (size_t)d.N * d.D * sizeof(uint16_t);
+  // without `need`: every region at its largest, so that one size serves every entry
+  // point and option; with it, only what that call uses
+  const bool int8 = !need || need->qk_int8;
+  const bool fp8 = !need || need->pv_fp8;
+  size_t conv = 0;
+  if (!need) {
+    const size_t vt8 = BH * (size_t)d.nK * 64 * d.D;
+    conv = 3 * one16 > vt8 ? 3 * one16 : vt8;
+  } else if (dtype == SPARGE_F32) {
+    conv = 3 * one16;                                     // Q, K and V rounded to 16 bits
+  } else if (need->pv_fp8) {
+    conv = BH * (size_t)d.nK * 64 * d.D;                  // E4M3 V tiles
+  } else if (dtype == SPARGE_BF16 && need->pv_fp16) {
+    conv = one16;                                         // V rounded to fp16
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
   w.qmean = take(BH * pad16(d.nQ) * d.D * sizeof(double));
@@ -25,18 +43,15 @@ Workspace plan_workspace(const Dims& d, int dtype) {
   w.scores = take(BH * d.nQ * d.nK * sizeof(double));
   w.lists = take(BH * d.nQ * d.lstride * sizeof(uint16_t));
   w.counts = take(BH * d.nQ * sizeof(int));
-  w.k8 = take(BH * (size_t)d.nK * 64 * d.D);
-  w.kscale = take(BH * d.nK * sizeof(float));
-  w.kbar = take(BH * d.nK * d.D * sizeof(float));
-  w.kc = take(BH * d.nK * 2 * d.D);
+  w.k8 = take(int8 ? BH * (size_t)d.nK * 64 * d.D : 0);
+  w.kscale = take(int8 ? BH * d.nK * sizeof(float) : 0);
+  w.kbar = take(int8 ? BH * d.nK * d.D * sizeof(float) : 0);
+  w.kc = take(int8 ? BH * d.nK * 2 * d.D : 0);
   w.kcs = take(BH * sizeof(float));
-  // fp32 inputs use 3 16-bit copies; fp8 P.V (16-bit inputs) its E4M3 V tiles
-  const size_t conv16 = 3 * BH * (size_t)d.N * d.D * sizeof(uint16_t);
-  const size_t vt8 = BH * (size_t)d.nK * 64 * d.D;
-  w.conv = take(conv16 > vt8 ? conv16 : vt8);
-  w.vmaxp = take(BH * d.nQ * d.D * sizeof(float));
-  w.vscale = take(BH * d.D * sizeof(float));
-  w.vinv = take(BH * d.D * sizeof(float));
+  w.conv = take(conv);
+  w.vmaxp = take(fp8 ? BH * d.nQ * d.D * sizeof(float) : 0);
+  w.vscale = take(fp8 ? BH * d.D * sizeof(float) : 0);
+  w.vinv = take(fp8 ? BH * d.D * sizeof(float) : 0);
   w.hparams = take(3 * (size_t)d.H * sizeof(double));
   w.counters = take(8 * sizeof(unsigned long long));
   w.total = off;
@@ -288,7 +303,6 @@ sparge_status run_predictor(Ctx& c, const sparge_tensor* q, const sparge_tensor*
 // those copies.
 sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
                      const sparge_tensor* v, const sparge_opts& o, Operands& op) {
-  const size_t one = (size_t)c.d.B * c.d.H * c.d.N * c.d.D;
   op.q = view_of(q);
   op.k = view_of(k);
   op.in_f16 = q->dtype == SPARGE_F16;
@@ -300,7 +314,7 @@ sparge_status prep16(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
   if (v_native || o.pv_fp8) {
     op.v = view_of(v);
   } else {
-    v16 = c.at<uint16_t>(c.w.conv) + 2 * one;
+    v16 = c.at<uint16_t>(c.w.conv);
     op.v = View{v16, (int64_t)c.d.H * c.d.N * c.d.D, (int64_t)c.d.N * c.d.D, (int64_t)c.d.D};
   }
   const int64_t chead = (int64_t)c.d.nK * 64 * c.d.D;
@@ -328,9 +342,9 @@ sparge_status run_select(Ctx& c, double topk, int cdf, int causal, const sparge_
 }
 
 sparge_status init_ctx(Ctx& c, const sparge_tensor* q, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, const PlanNeeds* need = nullptr) {
   c.d = dims_of(q);
-  c.w = plan_workspace(c.d, q->dtype);
+  c.w = plan_workspace(c.d, q->dtype, need);
   if (!workspace) return SPARGE_E_WORKSPACE;
   if (workspace_bytes < c.w.total) return SPARGE_E_WORKSPACE;
   if (((uintptr_t)workspace) % 256 != 0) return SPARGE_E_UNSUPPORTED;
@@ -368,22 +382,26 @@ size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
 
 namespace {
 
-// sparge_topk_attn (cdf = 0: sel is the kept fraction) and sparge_cdf_attn (cdf = 1:
-// sel is the softmax-mass threshold).
-sparge_status predicted_attn(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
-                             const sparge_tensor* out, double sel, int cdf, int32_t is_causal,
-                             const sparge_opts* opts, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+// Argument checks of sparge_topk_attn, sparge_cdf_attn and sparge_topk_attn_noalloc
+// (sel: the kept fraction or the softmax-mass threshold); fills the effective options.
+sparge_status check_predicted(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
+                              const sparge_tensor* out, double sel, const sparge_opts* opts,
+                              sparge_opts& o) {
   sparge_status st;
   if ((st = check_qkv(q, k, v, out)) != SPARGE_OK) return st;
   if ((st = check_opts(opts)) != SPARGE_OK) return st;
   if ((st = check_head_params(opts, q->H)) != SPARGE_OK) return st;
   if (!(sel > 0.0 && sel <= 1.0)) return SPARGE_E_ARG;
-  sparge_opts o;
   if (opts) o = *opts; else sparge_default_opts(&o);
   if (o.pv_fp8 && q->dtype == SPARGE_F32) return SPARGE_E_UNSUPPORTED;
-  Ctx c;
-  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  return SPARGE_OK;
+}
+
+// The launch sequence of the predicted-mask calls (cdf = 0: top-k, 1: threshold).
+sparge_status run_predicted(Ctx& c, const sparge_tensor* q, const sparge_tensor* k,
+                            const sparge_tensor* v, const sparge_tensor* out, double sel, int cdf,
+                            int32_t is_causal, const sparge_opts& o) {
+  sparge_status st;
   if ((st = begin_stats(c, &o)) != SPARGE_OK) return st;
   if ((st = stage_head_params(c, o)) != SPARGE_OK) return st;
   Operands op;
@@ -397,6 +415,55 @@ sparge_status predicted_attn(const sparge_tensor* q, const sparge_tensor* k, con
   if ((st = run_predictor(c, q, k, sel, cdf, is_causal != 0, o, o.mask_out)) != SPARGE_OK) return st;
   if ((st = run_attention(c, op, out, o, is_causal != 0, o.filter_on != 0)) != SPARGE_OK) return st;
   return end_stats(c, &o);
+}
+
+sparge_status predicted_attn(const sparge_tensor* q, const sparge_tensor* k, const sparge_tensor* v,
+                             const sparge_tensor* out, double sel, int cdf, int32_t is_causal,
+                             const sparge_opts* opts, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  sparge_status st;
+  sparge_opts o;
+  if ((st = check_predicted(q, k, v, out, sel, opts, o)) != SPARGE_OK) return st;
+  Ctx c;
+  if ((st = init_ctx(c, q, workspace, workspace_bytes, stream)) != SPARGE_OK) return st;
+  return run_predicted(c, q, k, v, out, sel, cdf, is_causal, o);
+}
+
+// Scratch of sparge_topk_attn_noalloc: static device storage of the library's code
+// object, so each GPU the library runs on holds its own copy for the life of the
+// process.  Host code never uses the array's name as an address: the address of a
+// device's copy is looked up once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = SPARGE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];
+
+// The address of the scratch copy of the device that `stream` belongs to (the current
+// device for the NULL stream).
+sparge_status scratch_for(hipStream_t stream, void** addr) {
+  int dev = -1;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return SPARGE_E_HIP;
+    dev = (int)sd;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return SPARGE_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SPARGE_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SPARGE_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SPARGE_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return SPARGE_E_HIP;
+    scratch_addr[dev] = p;
+  }
+  *addr = scratch_addr[dev];
+  return SPARGE_OK;
 }
 
 }  // namespace
@@ -416,6 +483,22 @@ sparge_status sparge_cdf_attn(const sparge_tensor* q, const sparge_tensor* k,
                               void* workspace, size_t workspace_bytes, void* stream) {
   return predicted_attn(q, k, v, out, cdf_threshold, 1, is_causal, opts, workspace,
                         workspace_bytes, stream);
+}
+
+sparge_status sparge_topk_attn_noalloc(const sparge_tensor* q, const sparge_tensor* k,
+                                       const sparge_tensor* v, const sparge_tensor* out, double topk,
+                                       int32_t is_causal, const sparge_opts* opts, void* stream) {
+  sparge_status st;
+  sparge_opts o;
+  if ((st = check_predicted(q, k, v, out, topk, opts, o)) != SPARGE_OK) return st;
+  // the regions this call uses, sized to it; beyond the scratch it cannot run
+  const PlanNeeds need{o.qk_int8 != 0, o.pv_fp16 != 0, o.pv_fp8 != 0};
+  if (plan_workspace(dims_of(q), q->dtype, &need).total > kScratchBytes) return SPARGE_E_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_for((hipStream_t)stream, &ws)) != SPARGE_OK) return st;
+  Ctx c;
+  if ((st = init_ctx(c, q, ws, kScratchBytes, stream, &need)) != SPARGE_OK) return st;
+  return run_predicted(c, q, k, v, out, topk, 0, is_causal, o);
 }
 
 sparge_status block_sparse_attn(const sparge_tensor* q, const sparge_tensor* k,

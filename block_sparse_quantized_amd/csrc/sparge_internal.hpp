@@ -66,7 +66,14 @@ struct Workspace {
   size_t total;
 };
 
-Workspace plan_workspace(const Dims& d, int dtype);
+// The options of one call that decide which optional regions it uses.
+struct PlanNeeds {
+  int qk_int8, pv_fp16, pv_fp8;
+};
+
+// need == nullptr: every region at its largest (one size for every entry point and
+// option); otherwise only the regions that call uses.
+Workspace plan_workspace(const Dims& d, int dtype, const PlanNeeds* need = nullptr);
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (return hipSuccess or the launch error).

@@ -140,6 +140,23 @@ sparge_status sparge_topk_attn(const sparge_tensor* q, const sparge_tensor* k,
                                double topk, int32_t is_causal, const sparge_opts* opts,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* sparge_topk_attn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument; the call's scratch regions (sized to its shape, dtype and options) live
+ * in the library's own static device storage of SPARGE_NOALLOC_SCRATCH_BYTES, one copy
+ * per GPU the library runs on, held until the process ends.  The call allocates
+ * nothing.  A problem whose regions exceed the scratch returns SPARGE_E_WORKSPACE
+ * before anything is queued (16-bit inputs of B=1, H=32, N=8192, D=128 fit under
+ * every option; N=131072 does not).  Every call on one GPU shares that GPU's scratch,
+ * which keeps the previous call's contents: calls that can overlap on one GPU
+ * (different streams, or threads without ordering) race on it and must not be made.
+ * Otherwise identical to sparge_topk_attn; the device is the stream's (the current
+ * device for the NULL stream). */
+#define SPARGE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+sparge_status sparge_topk_attn_noalloc(const sparge_tensor* q, const sparge_tensor* k,
+                                       const sparge_tensor* v, const sparge_tensor* out, double topk,
+                                       int32_t is_causal, const sparge_opts* opts, void* stream);
+
 /* Threshold variant of sparge_topk_attn (the meansim calls without topk, e.g.
  * spas_sage2_attn_meansim_cuda of [readme] "Avalible API" and [gittools] API list;
  * [chapterpal] recommendations on calibrating thresholds): identical except for the

@@ -3,7 +3,7 @@
 api.cpp (validation, workspace planning, launch sequencing) and hilbert.cpp (the
 host Hilbert order) are compiled by g++ with -fsanitize=address,undefined into a
 host-only library whose kernel launchers are stand-ins (tests/host/abi_host_stubs.cpp;
-no test here reaches a launch), and tests/test_abi.py runs against that library in
+no test here reaches a launch or a device lookup), and tests/test_abi.py runs against that library in
 a child process with the ASan runtime preloaded.  Any out-of-bounds access, use of
 freed memory or undefined behaviour on those paths aborts the child.
 """
@@ -35,6 +35,9 @@ def sanitized_lib():
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fPIC", "-shared",
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
+           # device-side spellings the host compiler lacks (the static scratch of the
+           # allocation-free entry point becomes ordinary host storage here)
+           "-D__align__(n)=__attribute__((aligned(n)))", "-DHIP_SYMBOL(x)=((const void*)&(x))",
            "-x", "c++", os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "hilbert.cpp"),
            os.path.join(ROOT, "tests", "host", "abi_host_stubs.cpp"),
            "-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}",
