@@ -430,6 +430,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--pv-fp8", action="store_true",
                     help="time the int8 Q.K^T / fp8 P.V path of the workload instead of its own")
+    ap.add_argument("--bf16", action="store_true",
+                    help="time the 16-bit path (bf16 Q.K^T and P.V) of the workload instead of its own")
     ap.add_argument("--cdf", type=float, default=None, metavar="TAU",
                     help="time the threshold selection (softmax mass TAU) instead of top-k")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -467,6 +469,8 @@ def main():
 
     if args.pv_fp8:
         path = Path(wl, dev, qk_int8=True, pv_fp16=False, pv_fp8=True, cdf=args.cdf)
+    elif args.bf16:
+        path = Path(wl, dev, qk_int8=False, pv_fp16=False, pv_fp8=False, cdf=args.cdf)
     else:
         path = Path(wl, dev, cdf=args.cdf)
     _, stats = path.step(stats=True)
@@ -495,7 +499,8 @@ def main():
             s16, a16, _ = time_path(p16, ev, max(3, args.steps // 2), 1)
             extras["bf16_variant"] = {"ms_per_step": round(s16, 3),
                                       "tops_dense_equiv": round(dense / (s16 * 1e-3) / 1e12, 2),
-                                      "roofline": roofline(st16, D, False, a16, None)}
+                                      "roofline": roofline(st16, D, False, a16,
+                                                           committed_traffic(wl.name, kernel_src, "bf16"))}
             del p16
         if wl.dtype != torch.float32 and not path.pv_fp8:   # fp8 P.V takes 16-bit inputs
             p8 = Path(wl, dev, qk_int8=True, pv_fp16=False, pv_fp8=True,
