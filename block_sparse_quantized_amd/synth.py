@@ -100,7 +100,9 @@ def _gaussian_taps(sigma: float, device) -> torch.Tensor:
 def smooth_field(white: torch.Tensor, sigma: float) -> torch.Tensor:
     """Separable Gaussian smoothing over every axis but the first, reflect borders.
 
-    ``white`` has shape (C, *grid); returns the same shape.
+    ``white`` has shape (C, *grid); returns the same shape.  Each axis is one fixed
+    sequence of elementwise products and sums over shifted copies (no convolution
+    library call), so every device rounds it the same way.
     """
     taps = _gaussian_taps(sigma, white.device)
     r = (taps.numel() - 1) // 2
@@ -109,21 +111,26 @@ def smooth_field(white: torch.Tensor, sigma: float) -> torch.Tensor:
     for ax in range(1, nd + 1):
         moved = out.movedim(ax, -1)
         shp = moved.shape
-        flat = moved.reshape(-1, 1, shp[-1])
-        pad = min(r, shp[-1] - 1)
+        L = shp[-1]
+        flat = moved.reshape(-1, 1, L)
+        pad = min(r, L - 1)
         flat = F.pad(flat, (pad, pad), mode="reflect")
         if pad < r:
             flat = F.pad(flat, (r - pad, r - pad), mode="replicate")
-        flat = F.conv1d(flat, taps.view(1, 1, -1))
-        out = flat.reshape(shp).movedim(-1, ax)
+        acc = taps[0] * flat[..., 0:L]
+        for t in range(1, 2 * r + 1):
+            acc = acc + taps[t] * flat[..., t:t + L]
+        out = acc.reshape(shp).movedim(-1, ax)
     return out
 
 
 def _standardise(x: torch.Tensor) -> torch.Tensor:
-    # x: (C, cells); zero mean, unit variance per channel
-    mu = x.mean(dim=1, keepdim=True)
-    sd = x.std(dim=1, unbiased=False, keepdim=True).clamp_min(1e-12)
-    return (x - mu) / sd
+    # x: (C, cells); zero mean, unit variance per channel (statistics in fp64, so a
+    # device's reduction order does not reach the fp32 result in practice)
+    xd = x.double()
+    mu = xd.mean(dim=1, keepdim=True)
+    sd = xd.std(dim=1, unbiased=False, keepdim=True).clamp_min(1e-12)
+    return ((xd - mu) / sd).float()
 
 
 def _head(wl: Workload, stream: int, b: int, h: int, device) -> torch.Tensor:
@@ -189,3 +196,12 @@ def checksum(t: torch.Tensor) -> str:
     """Stable hex digest of a tensor's bytes (detects generator drift)."""
     import hashlib
     return hashlib.sha256(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+
+
+def fingerprint(t: torch.Tensor) -> list:
+    """Three fp64 sums of a tensor, computed where it lives: of x, of x^2 and of
+    x * cos(flat index).  A change of seed or recipe moves them far more than
+    last-bit differences between devices do."""
+    x = t.detach().double().reshape(-1)
+    w = torch.cos(torch.arange(x.numel(), device=x.device, dtype=torch.float64))
+    return [float(x.sum()), float((x * x).sum()), float((x * w).sum())]

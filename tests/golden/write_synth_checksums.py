@@ -1,4 +1,4 @@
-"""Writes tests/golden/synth_checksums.json: SHA-256 prefixes of the seeded synthetic
+"""Writes tests/golden/synth_checksums.json: fingerprints of the seeded synthetic
 inputs (block_sparse_quantized_amd/synth.py), so that a change of generator, seed
 layout or torch RNG shows up as a failing test rather than as silently different
 workloads.
@@ -7,10 +7,12 @@ workloads.
     python tests/golden/write_synth_checksums.py cuda   # whole tensors, drawn on the GPU
     python tests/golden/write_synth_checksums.py cuda OUT.json   # write elsewhere
 
-The CPU entries cover one head per workload (every head has its own generator
-stream, so head (0, 0) of a one-head workload is head (0, 0) of the full one); the
-GPU entries cover the whole tensors that the GPU tests and bench.py draw on the
-device.  Each run updates only its own section.
+The CPU entries are SHA-256 prefixes of head (0, 0) of every workload (every head
+has its own generator stream, so head (0, 0) of a one-head workload is head (0, 0)
+of the full one).  The GPU entries are fp64 fingerprints (synth.fingerprint) of the
+whole tensors that the GPU tests and bench.py draw on the device, compared with a
+relative tolerance: a device's own reductions may move a last bit, a different seed
+or recipe moves them completely.  Each run updates only its own section.
 """
 import json
 import os
@@ -29,9 +31,10 @@ def digests(device):
         if device == "cpu":
             wl = synth.workload(name, B=1, H=1)
         q, k, v = synth.make_qkv(wl, device=device)
-        d = {"shape": list(q.shape), "q": synth.checksum(q), "k": synth.checksum(k), "v": synth.checksum(v)}
+        digest = synth.checksum if device == "cpu" else synth.fingerprint
+        d = {"shape": list(q.shape), "q": digest(q), "k": digest(k), "v": digest(v)}
         if wl.api == "block_sparse":
-            d["mask"] = synth.checksum(synth.make_block_mask(wl, device=device))
+            d["mask"] = digest(synth.make_block_mask(wl, device=device))
         res[name] = d
         del q, k, v
     return res
