@@ -190,6 +190,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// 16 bytes per lane from a raw buffer (resource r, this lane's byte offset) into LDS
+// at dst + 16 * lane (buffer_load_dwordx4 ... lds); offsets past the resource's
+// extent read as zeros.
+__device__ __forceinline__ void buffer_lds16(__amdgpu_buffer_rsrc_t r, lds_void_ptr dst, unsigned int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)voff, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -446,11 +453,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
   // Direct-to-LDS loads of one block's K tile (into K stage KS) or V tile (into V
   // stage VS): wavefront w issues chunks w, w+4, ... of the tile; lane l of chunk c
   // fills LDS bytes 1024c + 16l, i.e. row r = c*1024/ROW + l/G, physical granule
-  // l%G, holding logical granule (l%G) ^ f(r).  Rows past N (ragged last block)
-  // re-read row N-1; their scores are masked, so they contribute exactly zero.
-  // Per-lane byte offsets of this wavefront's chunks (c = 4cc + w) inside a full
-  // block; the block's base address is wave-uniform, so each load is a scalar base
-  // plus one 32-bit vector offset.
+  // l%G, holding logical granule (l%G) ^ f(r).
+  // Per-lane byte offsets of this wavefront's chunks (c = 4cc + w) inside a block;
+  // the block's base address is wave-uniform, so each load is a buffer resource in
+  // SGPRs plus one 32-bit vector offset.
   constexpr int KCW = KCHUNK / 4, VCW = VCHUNK / 4;
   unsigned int koff[KCW], voff[VCW];
 #pragma unroll
@@ -469,49 +475,35 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p, Dims 
       voff[cc] = (unsigned int)(r * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
     }
   }
-  // Block bases as 32 x 32 -> 64-bit products (row strides are below 4 GB); one
-  // wave-uniform branch per tile chooses the precomputed offsets (full block) or
-  // the clamped ones (the ragged last block).
+  // Each load is a raw buffer load to LDS (buffer_load_dwordx4 ... lds): a buffer
+  // resource over the block's own rows (base, byte extent) in SGPRs and this lane's
+  // 32-bit offset, so a full block and the ragged last one take the same
+  // instructions: rows past N lie outside the resource's extent and read as zeros
+  // (their scores are masked and their P is zero, so they contribute nothing).
+  // Block bases are 32 x 32 -> 64-bit products (row strides are below 4 GB).
+  constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
   const unsigned int ksrow32 = (unsigned int)ksrow, vsrow32 = (unsigned int)vsrow;
   auto dma_k = [&](int j, auto kstage) {
     unsigned char* dst = decltype(kstage)::value ? Ks1 : Ks0;
     const char* base = Kb + (uint64_t)(unsigned int)(64 * j) * ksrow32;
-    if (QK8 || 64 * j + 64 <= N) {
+    const int rows = QK8 ? 64 : min(64, N - 64 * j);   // int8 codes are padded to whole blocks
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, (short)0, (int)((unsigned int)(rows - 1) * ksrow32 + (unsigned int)KROW), kRsrcWord3);
 #pragma unroll
-      for (int cc = 0; cc < KCW; ++cc)
-        __builtin_amdgcn_global_load_lds((const void*)(base + koff[cc]),
-                                         (lds_void_ptr)(dst + 1024 * (4 * cc + w)), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < KCW; ++cc) {
-        const int c = 4 * cc + w;
-        const int r = c * (1024 / KROW) + lane / KG;
-        const unsigned int off =
-            (unsigned int)(min(r, N - 1 - 64 * j) * ksrow + 16 * ((lane % KG) ^ fkx<KG, PV8>(r)));
-        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
-      }
-    }
+    for (int cc = 0; cc < KCW; ++cc)
+      buffer_lds16(r, (lds_void_ptr)(dst + 1024 * (4 * cc + w)), koff[cc]);
   };
   auto dma_v = [&](int j, auto vstage) {
     unsigned char* dst = decltype(vstage)::value ? Vs1 : Vs0;
     // fp8 tiles are whole (tokens past N are stored as zeros)
     const char* base = PV8 ? Vb + (uint64_t)(unsigned int)j * (64 * D)
                            : Vb + (uint64_t)(unsigned int)(64 * j) * vsrow32;
-    if (PV8 || 64 * j + 64 <= N) {
+    const unsigned int extent = PV8 ? (unsigned int)(64 * D)
+                                    : (unsigned int)(min(64, N - 64 * j) - 1) * vsrow32 + (unsigned int)VROW;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)extent, kRsrcWord3);
 #pragma unroll
-      for (int cc = 0; cc < VCW; ++cc)
-        __builtin_amdgcn_global_load_lds((const void*)(base + voff[cc]),
-                                         (lds_void_ptr)(dst + 1024 * (4 * cc + w)), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < VCW; ++cc) {
-        const int c = 4 * cc + w;
-        const int r = c * (1024 / VROW) + lane / VG;
-        const unsigned int off =
-            (unsigned int)(min(r, N - 1 - 64 * j) * vsrow + 16 * ((lane % VG) ^ fv<VG>(r)));
-        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_ptr)(dst + 1024 * c), 16, 0, 0);
-      }
-    }
+    for (int cc = 0; cc < VCW; ++cc)
+      buffer_lds16(r, (lds_void_ptr)(dst + 1024 * (4 * cc + w)), voff[cc]);
   };
 
   // per-lane row of the Q.K^T A fragments, granule 2s+hf: 32kt + swap23(ql), or for

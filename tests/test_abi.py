@@ -41,6 +41,15 @@ def test_exports_every_declared_symbol(lib):
     assert lib.sparge_abi_version() == 3
 
 
+def test_every_symbol_resolves_at_load():
+    """Binding every symbol when the library loads (RTLD_NOW) fails on any undefined
+    one, e.g. a kernel's host launch stub that the host pass did not emit, which a
+    lazily bound load would only report at the first launch."""
+    ctypes.CDLL(L.lib_path(), mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.lib_path()], capture_output=True, text=True).stdout
+    assert "device_stub" not in out
+
+
 def test_struct_layout_matches_c_compiler():
     prog = r'''
 #include <stdio.h>
