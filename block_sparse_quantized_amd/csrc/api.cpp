@@ -78,6 +78,8 @@ sparge_status check_tensor(const sparge_tensor* t) {
   if (((uintptr_t)t->data) % 16 != 0) return SPARGE_E_UNSUPPORTED;
   if (t->sB < 0 || t->sH < 0 || t->sN < 0) return SPARGE_E_UNSUPPORTED;
   if ((t->sB * es) % 16 || (t->sH * es) % 16 || (t->sN * es) % 16) return SPARGE_E_UNSUPPORTED;
+  // a 64-row block of K or V is addressed with 32-bit byte offsets
+  if (t->sN * es >= ((int64_t)1 << 26)) return SPARGE_E_UNSUPPORTED;
   return SPARGE_OK;
 }
 

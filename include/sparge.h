@@ -15,7 +15,9 @@
  *   - Tensors are described by sparge_tensor: logical shape (B, H, N, D) as in
  *     torch's scaled_dot_product_attention ("drop-in replacement" for it,
  *     [topgit] "Key features"), element strides for B, H and N, and a unit stride
- *     for D.  Row starts and the data pointer must be 16-byte aligned.
+ *     for D.  Row starts and the data pointer must be 16-byte aligned, and the N
+ *     stride must stay below 64 MiB (the attention kernel addresses a 64-row block
+ *     with 32-bit offsets); otherwise SPARGE_E_UNSUPPORTED.
  *   - q, k, v and out share one dtype and one (B, H, N, D); D is 64 or 128;
  *     1 <= N <= 262144.  fp32 inputs are read exactly by the predictor and rounded to
  *     bfloat16 for the attention products; out is written in the input dtype.

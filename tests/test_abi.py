@@ -103,6 +103,7 @@ def test_validation_errors_topk(lib):
     assert call_topk(lib, q, k, v, T(data=FAKE)) == -4                     # out aliases q
     assert call_topk(lib, T(data=FAKE + 2), k, v, o) == -5                 # misaligned
     assert call_topk(lib, T(sN=65), k, v, o) == -5                         # row stride not 16B
+    assert call_topk(lib, q, T(sN=1 << 25, data=FAKE + 4096), v, o) == -5  # row stride of 64 MiB
     assert call_topk(lib, q, k, v, o, ws=None) == -6
     assert call_topk(lib, q, k, v, o, wsb=1024) == -6
     bad = L.SpargeOpts()
