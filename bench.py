@@ -450,7 +450,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the path shards over (batch, head) with no "
-              f"communication and multi-GPU runs are not part of this build; got --gpus {args.gpus}",
+              f"communication, and this benchmark does not run several GPUs; got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 
