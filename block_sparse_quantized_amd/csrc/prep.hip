@@ -18,7 +18,8 @@
 // One workgroup of 256 threads per (b, h, Q block i): Q rows 128i..128i+127, the
 // K blocks 2i and 2i+1 over the same rows, and the same V rows.  Every 16-byte
 // chunk of the three tiles is loaded once, up front (coalesced: sixteen (D=128)
-// or eight (D=64) consecutive lanes read one row), and kept in registers.  Row
+// or eight (D=64) consecutive lanes read one row; raw buffer loads, so rows past N
+// read as zeros without a predicate), and kept in registers.  Row
 // norms come from the registers (lane partials, then a reduction across the
 // row's lanes); the channel pass reads a copy of the tile in LDS (row pitch
 // padded by 16 bytes); the int8 codes come from the registers again and leave
@@ -31,6 +32,7 @@ namespace sparge {
 namespace {
 
 constexpr int kPad = 16;  // bytes of padding per LDS tile row
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer resource: 32-bit data format
 
 __device__ __forceinline__ float u16_to_f32(unsigned short u, bool f16) {
   return f16 ? (float)__builtin_bit_cast(_Float16, u) : __uint_as_float((unsigned int)u << 16);
@@ -97,19 +99,36 @@ __global__ __launch_bounds__(256) void prep_kernel(View q, View k, View v, Dims 
   const int r0 = 128 * i;
   const int nrows = min(128, N - r0);
 
-  // every chunk of the three tiles, issued before any arithmetic
+  // every chunk of the three tiles, issued before any arithmetic.  Chunk kk of a thread
+  // is row tid / CH + RPK kk: each slab of RPK rows is read by raw buffer loads over a
+  // resource that spans the slab's rows below N (base, byte extent), so rows past N
+  // read as zeros with no predicate and no 64-bit address per lane; the lane offsets
+  // stay below 2^31 because row strides are below 64 MiB.
+  constexpr int RPK = 256 / CH;           // rows per slab
   uint4 qr[NCH], kr[NCH], vr[NCH];
-  const unsigned short* qb = (const unsigned short*)q.p + (int64_t)b * q.sB + (int64_t)h * q.sH;
-  const unsigned short* kb = (const unsigned short*)k.p + (int64_t)b * k.sB + (int64_t)h * k.sH;
-  const unsigned short* vb = (const unsigned short*)v.p + (int64_t)b * v.sB + (int64_t)h * v.sH;
+  const int lrow = tid / CH, lch = tid % CH;
+  struct Slabs {
+    const char* base;   // row r0 of this (b, h)
+    int rowb;           // bytes per row
+  };
+  auto slabs = [&](const View& x) {
+    return Slabs{(const char*)x.p + 2 * ((int64_t)b * x.sB + (int64_t)h * x.sH + (int64_t)r0 * x.sN),
+                 (int)(2 * x.sN)};
+  };
+  auto slab_load = [&](const Slabs& s, int kk) -> uint4 {
+    const int rows = min(RPK, nrows - RPK * kk);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(s.base + (int64_t)(RPK * kk) * s.rowb), (short)0,
+        rows > 0 ? (rows - 1) * s.rowb + 2 * D : 0, kRsrcWord3);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, lrow * s.rowb + 16 * lch, 0, 0);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  const Slabs qs = slabs(q), ks = slabs(k), vs = slabs(v);
 #pragma unroll
   for (int kk = 0; kk < NCH; ++kk) {
-    const int e = tid + 256 * kk, row = e / CH, ch = e % CH;
-    const bool ok = row < nrows;
-    const int64_t rr = r0 + row;
-    qr[kk] = ok ? *(const uint4*)(qb + rr * q.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
-    kr[kk] = ok ? *(const uint4*)(kb + rr * k.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
-    if constexpr (VCONV) vr[kk] = ok ? *(const uint4*)(vb + rr * v.sN + 8 * ch) : make_uint4(0, 0, 0, 0);
+    qr[kk] = slab_load(qs, kk);
+    kr[kk] = slab_load(ks, kk);
+    if constexpr (VCONV) vr[kk] = slab_load(vs, kk);
   }
 
   // V, fp8 P.V: per-channel max |v| over the block's rows (each thread's chunk is 8
